@@ -1,0 +1,110 @@
+"""CPU attention oracle: TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  It shares no code with the GPU library and never touches device
+memory.  ``attention_rows`` wraps the fp64 C implementation in ``oracle.c``
+(the plain definition, score rows materialised); ``online_softmax`` holds the
+recurrence the pages derive, used only to check it against the definition.
+
+Every function here is pinned by tests against values the pages print, closed
+forms and brute force on tiny inputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` with gcc (fp64, OpenMP, no fast-math)."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+           "-std=c11", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                build(force=False)
+            lib = ctypes.CDLL(_LIB_PATH)
+            lib.oracle_attention_rows.restype = ctypes.c_int
+            lib.oracle_attention_rows.argtypes = [
+                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                ctypes.c_void_p, ctypes.c_void_p]
+            lib.oracle_num_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle runs on."""
+    return int(_load().oracle_num_threads())
+
+
+def attention_rows(q, k, v, scale: float, causal: bool, rows=None):
+    """Exact attention for selected query rows, in fp64.
+
+    ``q, k, v``: uint16 bfloat16 bit arrays shaped [B, H, N, d] (contiguous).
+    ``scale``: the softmax scale (a Python float; pass the fp32 value the GPU
+    receives, widened).  ``rows``: flat row ids ``(b*H + h)*N + i``; ``None``
+    means every row.  Returns ``(out [nrows, d] float64, lse [nrows] float64)``.
+    """
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    B, H, N, d = q.shape
+    if rows is None:
+        rows = np.arange(B * H * N, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, d), dtype=np.float64)
+    lse = np.empty(rows.size, dtype=np.float64)
+    rc = _load().oracle_attention_rows(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, N, d, float(scale), int(bool(causal)),
+        rows.ctypes.data, rows.size, out.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_attention_rows failed with code %d" % rc)
+    return out, lse
+
+
+def attention_f64(q, k, v, scale: float, causal: bool):
+    """Convenience for tiny hand-made cases: fp64 arrays (q [Nq, d], k and v
+    [N, d], Nq <= N) whose values are exactly representable in bfloat16
+    (checked), one head.  Query rows beyond Nq are zero padding and are not
+    returned; query row i is at position i for the causal rule."""
+    from inputs import f64_to_bf16_bits, bf16_bits_to_f64  # seeded-input helpers only
+    q = np.atleast_2d(np.asarray(q, dtype=np.float64))
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    nq, n = q.shape[0], k.shape[0]
+    if nq > n or k.shape != v.shape or q.shape[1] != k.shape[1]:
+        raise ValueError("need q [Nq, d], k and v [N, d] with Nq <= N")
+    qp = np.zeros_like(k)
+    qp[:nq] = q
+    arrs = []
+    for a in (qp, k, v):
+        bits = f64_to_bf16_bits(a)
+        if not np.array_equal(bf16_bits_to_f64(bits), a):
+            raise ValueError("value not exactly representable in bfloat16")
+        arrs.append(bits.reshape(1, 1, *a.shape))
+    return attention_rows(*arrs, scale=scale, causal=causal, rows=np.arange(nq))

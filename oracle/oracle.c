@@ -1,0 +1,121 @@
+/*
+ * Attention oracle: TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct CPU implementation of exact attention in
+ * fp64.  Only the tests, the smoke check and the benchmark's CPU-baseline leg
+ * may load it; the GPU library never does, and the two share no code.
+ *
+ * What it computes (for every requested query row i of head (b, h)):
+ *
+ *   s_j   = scale * sum_c q[i][c] * k[j][c]          for every permitted key j
+ *   m     = max_j s_j
+ *   l     = sum_j exp(s_j - m)
+ *   P_j   = exp(s_j - m) / l
+ *   O[c]  = sum_j P_j * v[j][c]
+ *   LSE   = m + ln(l)
+ *
+ * which is the attention rule softmax(Q K^T / sqrt(d)) V of "4 Triton and
+ * Custom Kernels" (aisyseng.dev), section 4.7, equation 4.1, with the scale
+ * passed in explicitly, evaluated with the "safe softmax" of the page
+ * "FlashAttention and kernels" (gtadkapally.com), section "Softmax, the safe way" (subtract the row
+ * maximum, then exponentiate, sum and divide).  The log-sum-exp side output is
+ * the natural log of the softmax denominator of the scaled scores, L = m + log(l)
+ * (same page, section "FlashAttention's forward pass", step 4).
+ *
+ * Permitted keys: all j in [0, N), or j <= i when causal (a token may attend to
+ * itself and earlier tokens only; same page, its glossary entry "causal mask").
+ *
+ * The score row of each query is materialised in full before the softmax, as in
+ * the naive three-step attention that "FlashAttention and kernels" contrasts with
+ * FlashAttention (section "What naive attention actually does").  Sums run over ascending indices.
+ * Inputs are bfloat16 bit patterns; widening bfloat16 to fp64 is exact.
+ * Built without -ffast-math.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* bfloat16 is the upper half of an IEEE binary32 value. */
+static double oracle_bf16_to_f64(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/*
+ * rows: flat row ids r = (b * H + h) * N + i, any order, each in [0, B*H*N).
+ * out:  nrows * d doubles (row-major), lse: nrows doubles.
+ * Returns 0 on success, 1 on a bad argument, 2 if scratch memory is exhausted.
+ */
+int oracle_attention_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                          int64_t B, int64_t H, int64_t N, int64_t d, double scale,
+                          int causal, const int64_t *rows, int64_t nrows,
+                          double *out, double *lse) {
+  if (!q || !k || !v || !rows || !out || !lse) return 1;
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || nrows < 0) return 1;
+  const int64_t total_rows = B * H * N;
+  for (int64_t t = 0; t < nrows; ++t)
+    if (rows[t] < 0 || rows[t] >= total_rows) return 1;
+
+  int failed = 0;
+#pragma omp parallel
+  {
+    double *s = (double *)malloc((size_t)N * sizeof(double));
+    double *qi = (double *)malloc((size_t)d * sizeof(double));
+    if (!s || !qi) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t t = 0; t < nrows; ++t) {
+        const int64_t r = rows[t];
+        const int64_t head = r / N;      /* b * H + h */
+        const int64_t i = r % N;         /* query position */
+        const uint16_t *kh = k + head * N * d;
+        const uint16_t *vh = v + head * N * d;
+        const int64_t nkeys = causal ? i + 1 : N;  /* keys 0 .. nkeys-1 */
+
+        for (int64_t c = 0; c < d; ++c) qi[c] = oracle_bf16_to_f64(q[r * d + c]);
+
+        /* 1. scores of the permitted keys */
+        for (int64_t j = 0; j < nkeys; ++j) {
+          double acc = 0.0;
+          for (int64_t c = 0; c < d; ++c) acc += qi[c] * oracle_bf16_to_f64(kh[j * d + c]);
+          s[j] = scale * acc;
+        }
+        /* 2. row maximum */
+        double m = s[0];
+        for (int64_t j = 1; j < nkeys; ++j)
+          if (s[j] > m) m = s[j];
+        /* 3. denominator */
+        double l = 0.0;
+        for (int64_t j = 0; j < nkeys; ++j) l += exp(s[j] - m);
+        /* 4. probabilities, 5. weighted sum of the value rows */
+        double *o = out + t * d;
+        for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+        for (int64_t j = 0; j < nkeys; ++j) {
+          const double p = exp(s[j] - m) / l;
+          for (int64_t c = 0; c < d; ++c) o[c] += p * oracle_bf16_to_f64(vh[j * d + c]);
+        }
+        /* 6. log-sum-exp of the scaled scores, natural log */
+        lse[t] = m + log(l);
+      }
+    }
+    free(s);
+    free(qi);
+  }
+  return failed ? 2 : 0;
+}
