@@ -1,0 +1,198 @@
+"""Throughput of the gfx950 FlashAttention-2 forward on one MI355X.
+
+One step = one non-causal and one causal forward pass over the B=4, H=8,
+N=4096, d=64 bf16 workload (the shape the article "How to profile and optimise
+kernels" benchmarks, section "Where the last article left off" and Round 5),
+inputs already resident in HBM.  Prints ONE JSON line:
+
+  value      TFLOP/s of the whole step, FLOPs = 4*B*H*N^2*d per mode, halved
+             for causal;
+  roofline   the dominant (non-causal) kernel against the bf16 dense MFMA peak,
+             its duration taken from HIP events on the launch stream;
+  cpu_baseline  the fp64 CPU oracle on a bounded row sample of the same
+             workload, on this host's cores (a baseline, not a target), with
+             the parity of those rows against the GPU output.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3|4|5]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd TFLOP/s (bf16, causal + non-causal) and % of bf16 MFMA peak"
+# The pages' figures for this exact workload (RTX 4070 SUPER, Triton): 1.954 ms
+# non-causal and 1.077 ms causal, i.e. 206.16 GFLOP in 3.031 ms.
+PAGES_STEP_TFLOPS = (4 * 32 * 4096 ** 2 * 64 * 1.5) / 3.031e-3 / 1e12
+
+
+def flops(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--cfg", type=str, default=None, help="force a tile variant: qb,waves,bk")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows-per-head", type=int, default=None)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads shard across GPUs with no exchange; see the design notes). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import flashattention_forward_fa2_amd as fa
+    import inputs
+
+    fa.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = inputs.WORKLOADS[args.workload]
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    modes = list(w["modes"]) if args.workload != 3 else [0, 1]
+    scale = inputs.default_scale(d)
+    cfg = tuple(int(x) for x in args.cfg.split(",")) if args.cfg else None
+
+    t0 = time.time()
+    q_bits, k_bits, v_bits = inputs.make_qkv(args.workload)
+    print("[bench] inputs %s generated in %.1fs" % (w["name"], time.time() - t0), file=sys.stderr, flush=True)
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
+    outs = {c: torch.empty_like(q) for c in modes}
+    lses = {c: torch.empty((B, H, N), dtype=torch.float32, device=dev) for c in modes}
+    stream = torch.cuda.current_stream(dev)
+
+    def launch(c):
+        fa.fa_fwd(q, k, v, scale=scale, causal=bool(c), out=outs[c], lse=lses[c], stream=stream, cfg=cfg)
+
+    # Warm-up: the requested steps, then keep the GPU busy ~1 s so clocks ramp.
+    for _ in range(max(1, args.warmup)):
+        for c in modes:
+            launch(c)
+    torch.cuda.synchronize()
+    t_end = time.time() + 1.0
+    while time.time() < t_end:
+        for c in modes:
+            launch(c)
+        torch.cuda.synchronize()
+
+    # Timed region: exactly K steps, HIP events around every kernel on its stream.
+    ev = {c: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for c in modes}
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        for c in modes:
+            ev[c][s][0].record(stream)
+            launch(c)
+            ev[c][s][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    step_flops = sum(flops(B, H, N, d, c) for c in modes)
+    ms_per_step = wall * 1e3 / args.steps
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    per_mode = {}
+    for c in modes:
+        ms = np.array([a.elapsed_time(b) for a, b in ev[c]])
+        avg = float(ms.mean())
+        tf = flops(B, H, N, d, c) / (avg * 1e-3) / 1e12
+        per_mode["causal" if c else "noncausal"] = dict(
+            kernel_ms_avg=round(avg, 5), kernel_ms_median=round(float(np.median(ms)), 5),
+            kernel_ms_min=round(float(ms.min()), 5), tflops=round(tf, 2),
+            frac_of_peak=round(tf / PEAK_BF16_TFLOPS, 4),
+            hbm_gbs=round((8.0 * B * H * N * d + 4.0 * B * H * N) / (avg * 1e-3) / 1e9, 1),
+            cfg=list(cfg if cfg else fa.default_cfg(N, d, bool(c))))
+    dom_c = max(modes, key=lambda c: per_mode["causal" if c else "noncausal"]["kernel_ms_avg"])
+    dom = per_mode["causal" if dom_c else "noncausal"]
+    roofline = dict(bound="mfma", achieved=dom["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=dom["frac_of_peak"], traffic=None,
+                    kernel="fa_fwd_kernel d=%d causal=%d cfg=%s" % (d, dom_c, dom["cfg"]),
+                    flops_per_launch=flops(B, H, N, d, dom_c))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, w, modes, q_bits, k_bits, v_bits, scale, outs, lses)
+
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / PAGES_STEP_TFLOPS, 3) if args.workload == 3 else None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "%s %s" % (w["name"], "+".join("causal" if c else "non-causal" for c in modes)),
+                   "B": B, "H": H, "N": N, "d": d, "scale": scale, "sigma_qk": w["sigma_qk"],
+                   "flops_per_step": step_flops, "modes": per_mode},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(args, w, modes, q_bits, k_bits, v_bits, scale, outs, lses):
+    """The oracle, as it stands, on a bounded row sample of the same workload."""
+    import torch
+    import oracle
+    from inputs import bf16_bits_to_f64, sample_rows, workload_seed
+
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    # About 16 GFLOP of fp64 oracle work (seconds on a many-core host).
+    mode_weight = sum(0.5 if c else 1.0 for c in modes)
+    per_head = args.cpu_rows_per_head or int(np.clip(16e9 / (B * H * 4.0 * N * d * mode_weight), 16, N))
+    rows = sample_rows(workload_seed(args.workload, 3), B, H, N, per_head=per_head)
+    i = rows % N
+    total_flops, total_s = 0.0, 0.0
+    parity = {}
+    for c in modes:
+        t0 = time.perf_counter()
+        o_ref, l_ref = oracle.attention_rows(q_bits, k_bits, v_bits, scale, bool(c), rows)
+        total_s += time.perf_counter() - t0
+        nkeys = (i + 1) if c else np.full(rows.shape, N)
+        total_flops += float(np.sum(4.0 * nkeys * d))
+        o = bf16_bits_to_f64(outs[c].view(torch.int16).cpu().numpy().view(np.uint16)).reshape(-1, d)[rows]
+        L = lses[c].cpu().numpy().reshape(-1)[rows]
+        err = np.abs(o - o_ref)
+        parity["causal" if c else "noncausal"] = dict(
+            max_abs=float(err.max()), mean_abs=float(err.mean()),
+            lse_rel=float((np.abs(L - l_ref) / np.maximum(1.0, np.abs(l_ref))).max()))
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return dict(value=round(total_flops / total_s / 1e12, 6), unit="TFLOP/s", cores=oracle.num_threads(),
+                kind="oracle",
+                sample="%d rows (%d per head, fixed edge rows + seeded) of %s, modes %s; fp64, %.1f GFLOP in %.2fs"
+                       % (rows.size, per_head, w["name"], modes, total_flops / 1e9, total_s),
+                cpu_model=cpu_model, parity_on_sample=parity)
+
+
+if __name__ == "__main__":
+    main()

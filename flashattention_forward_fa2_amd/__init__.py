@@ -1,0 +1,157 @@
+"""MI355X (gfx950) FlashAttention-2 forward: Python binding of libfa_fwd.so.
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+library; PyTorch supplies device memory and the stream.  There is no fallback:
+if the library is not built, or the device is not a gfx950, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+from .buildlib import LIB, build  # noqa: F401
+
+__all__ = ["fa_fwd", "fa_fwd_ptr", "fa_fwd_cfg", "FaError", "strerror", "version", "default_cfg",
+           "variants", "load_library", "EXPORTED_SYMBOLS"]
+
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_cfg", "fa_default_cfg", "fa_num_variants", "fa_variant",
+                    "fa_strerror", "fa_version")
+
+STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD_DIM", 4: "FA_ERR_SCALE",
+          5: "FA_ERR_ARG", 6: "FA_ERR_ALIGN", 7: "FA_ERR_ALIAS", 8: "FA_ERR_NO_DEVICE",
+          9: "FA_ERR_LAUNCH", 10: "FA_ERR_INTERNAL"}
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s (%d): %s" % (STATUS.get(status, "?"), status, msg))
+        self.status = status
+
+
+class TileCfg(ctypes.Structure):
+    _fields_ = [("qb", ctypes.c_int), ("waves", ctypes.c_int), ("bk", ctypes.c_int)]
+
+    def as_tuple(self):
+        return (self.qb, self.waves, self.bk)
+
+
+_lock = threading.Lock()
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+
+
+def load_library():
+    """Load libfa_fwd.so from the package directory (raises if it is not built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB):
+                raise FaError(10, "libfa_fwd.so is not built; run flashattention_forward_fa2_amd.build()")
+            lib = ctypes.CDLL(LIB)
+            fwd_args = [_P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _I, _P]
+            lib.fa_fwd.argtypes = fwd_args
+            lib.fa_fwd.restype = _I
+            lib.fa_fwd_cfg.argtypes = fwd_args + [ctypes.POINTER(TileCfg)]
+            lib.fa_fwd_cfg.restype = _I
+            lib.fa_default_cfg.argtypes = [_I, _I, _I, ctypes.POINTER(TileCfg)]
+            lib.fa_default_cfg.restype = _I
+            lib.fa_num_variants.argtypes = []
+            lib.fa_num_variants.restype = _I
+            lib.fa_variant.argtypes = [_I, ctypes.POINTER(_I), ctypes.POINTER(_I), ctypes.POINTER(TileCfg)]
+            lib.fa_variant.restype = _I
+            lib.fa_strerror.argtypes = [_I]
+            lib.fa_strerror.restype = ctypes.c_char_p
+            lib.fa_version.argtypes = []
+            lib.fa_version.restype = _I
+            _lib = lib
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return load_library().fa_strerror(int(status)).decode()
+
+
+def version() -> int:
+    return int(load_library().fa_version())
+
+
+def _check(status: int):
+    if status != 0:
+        raise FaError(status, strerror(status))
+
+
+def default_cfg(N: int, d: int, causal: bool):
+    c = TileCfg()
+    _check(load_library().fa_default_cfg(int(N), int(d), int(bool(causal)), ctypes.byref(c)))
+    return c.as_tuple()
+
+
+def variants():
+    """Compiled variants as (d, causal, (qb, waves, bk)) tuples."""
+    lib = load_library()
+    out = []
+    for i in range(lib.fa_num_variants()):
+        d, c, cfg = _I(), _I(), TileCfg()
+        _check(lib.fa_variant(i, ctypes.byref(d), ctypes.byref(c), ctypes.byref(cfg)))
+        out.append((d.value, c.value, cfg.as_tuple()))
+    return out
+
+
+def fa_fwd_ptr(q: int, k: int, v: int, out: int, lse: int, B: int, H: int, N: int, d: int,
+               scale: float, causal: bool, stream: int = 0, cfg=None) -> int:
+    """Raw-pointer call; returns the library's status code (does not raise)."""
+    lib = load_library()
+    args = (_P(q), _P(k), _P(v), _P(out), _P(lse), int(B), int(H), int(N), int(d),
+            ctypes.c_float(scale), int(causal), _P(stream))
+    if cfg is None:
+        return int(lib.fa_fwd(*args))
+    c = TileCfg(*cfg)
+    return int(lib.fa_fwd_cfg(*args, ctypes.byref(c)))
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+def fa_fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse=None,
+           stream=None, cfg=None):
+    """Attention forward on torch bf16 tensors [B, H, N, d] (contiguous, one device).
+
+    Returns ``(out, lse)``: ``out`` bf16 [B, H, N, d], ``lse`` fp32 [B, H, N].
+    ``scale`` defaults to the fp32 value of 1/sqrt(d).  Enqueued on ``stream``
+    (default: the current stream); no synchronisation.
+    """
+    import torch
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous bfloat16 device tensors")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 tensor [B, H, N]")
+    st = fa_fwd_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    B, H, N, d, scale, causal, _stream_handle(stream, q.device), cfg)
+    _check(st)
+    return out, lse
+
+
+def fa_fwd_cfg(q, k, v, cfg, scale: float | None = None, causal: bool = False, out=None, lse=None,
+               stream=None):
+    """``fa_fwd`` with an explicit ``(qb, waves, bk)`` tile configuration."""
+    return fa_fwd(q, k, v, scale=scale, causal=causal, out=out, lse=lse, stream=stream, cfg=tuple(cfg))

@@ -1,0 +1,58 @@
+"""Shared helpers of the GPU parity tests: move seeded bf16 inputs to the device,
+run the HIP path through the C ABI, and compare with the CPU oracle."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+
+from inputs import bf16_bits_to_f64
+
+# Tolerances on bf16 outputs against the fp64 oracle (element by element over
+# every compared row): max |dO| <= 2e-2, mean |dO| <= 2e-3; LSE: |dLSE| <=
+# 1e-4 * max(1, |LSE|) (a pure relative bound is ill-posed where LSE ~ 0).
+O_MAX_ABS = 2e-2
+O_MEAN_ABS = 2e-3
+LSE_REL = 1e-4
+
+
+def to_device(bits: np.ndarray, device="cuda:0"):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def gpu_forward(q_bits, k_bits, v_bits, scale, causal, cfg=None, device="cuda:0"):
+    import torch
+    import flashattention_forward_fa2_amd as fa
+    q, k, v = (to_device(a, device) for a in (q_bits, k_bits, v_bits))
+    out, lse = fa.fa_fwd(q, k, v, scale=scale, causal=causal, cfg=cfg)
+    torch.cuda.synchronize()
+    o = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    return o, lse.cpu().numpy()
+
+
+def compare(o_gpu_bits, lse_gpu, o_ref, lse_ref, rows=None, label=""):
+    """Element-wise comparison; returns the error summary, raises on failure."""
+    d = o_ref.shape[-1]
+    o = bf16_bits_to_f64(o_gpu_bits).reshape(-1, d)
+    L = np.asarray(lse_gpu, dtype=np.float64).reshape(-1)
+    if rows is not None:
+        o = o[rows]
+        L = L[rows]
+    err = np.abs(o - o_ref)
+    lerr = np.abs(L - lse_ref) / np.maximum(1.0, np.abs(lse_ref))
+    s = dict(max_abs=float(err.max()), mean_abs=float(err.mean()), lse_rel=float(lerr.max()),
+             finite=bool(np.all(np.isfinite(o)) and np.all(np.isfinite(L))), rows=int(o.shape[0]))
+    print("[parity] %s max|dO|=%.3e mean|dO|=%.3e max dLSE/max(1,|LSE|)=%.3e rows=%d"
+          % (label, s["max_abs"], s["mean_abs"], s["lse_rel"], s["rows"]), file=sys.stderr, flush=True)
+    assert s["finite"], "non-finite output"
+    assert s["max_abs"] <= O_MAX_ABS, s
+    assert s["mean_abs"] <= O_MEAN_ABS, s
+    assert s["lse_rel"] <= LSE_REL, s
+    return s
+
+
+def fp32_scale(d: int) -> float:
+    return float(np.float32(1.0 / math.sqrt(d)))
