@@ -14,7 +14,9 @@ LIB = os.path.join(PKG, "libfa_fwd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 instructions are switched off for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # MFMA accumulators in VGPRs: no AGPR<->VGPR copies around the rescale
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def build(verbose: bool = False, extra=()) -> str:

@@ -52,7 +52,7 @@ const Variant* find_variant(int d, int causal, const fa_tile_cfg& c) {
   return nullptr;
 }
 
-fa_tile_cfg default_cfg(int /*N*/, int /*d*/, int /*causal*/) { return fa_tile_cfg{1, 4, 64}; }
+fa_tile_cfg default_cfg(int /*N*/, int /*d*/, int /*causal*/) { return fa_tile_cfg{1, 8, 64}; }
 
 bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);

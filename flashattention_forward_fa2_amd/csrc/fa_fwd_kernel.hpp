@@ -15,17 +15,22 @@
 //
 // Scores stay in registers; the N x N matrix never reaches HBM.
 //
-// Layout choices (gfx950 MFMA, v_mfma_f32_32x32x16_bf16):
-// * S^T = K Q^T: the A operand is a K row segment (16 contiguous bytes of a key,
-//   read from LDS), the B operand a Q row segment held in VGPRs for the whole
+// gfx950 mapping (v_mfma_f32_32x32x16_bf16, accumulators in VGPRs):
+// * S^T = K Q^T: the A operand is a 16-byte K row segment read from LDS
+//   (ds_read_b128), the B operand a Q row segment held in VGPRs for the whole
 //   sweep.  The 32x32 fp32 result gives each lane ONE query (lane % 32) and 16
 //   keys, so the row max and row sum are in-lane reductions plus one
 //   v_permlane32_swap between the two lane halves.
-// * O^T += V^T P^T: the probabilities of a lane's query, packed to bf16, are
-//   already laid out as the B operand; V enters as the A operand from a V^T copy
-//   in LDS (transposed while being staged), whose key order inside each 16-key
-//   step matches the order in which the S^T accumulator holds the keys.  The
-//   alpha rescale of O is a per-lane scalar multiply.
+// * O^T += V^T P^T: a lane's probabilities, packed to bf16, are already laid out
+//   as the B operand.  V stays row-major in LDS and enters as the A operand
+//   through ds_read_b64_tr_b16, which hands each lane one head-dim column of a
+//   4-key x 16-column block; the key order inside each 16-key step matches the
+//   order in which the S^T accumulator holds the keys.  The alpha rescale of O
+//   is a per-lane scalar multiply, skipped when no lane's maximum moved.
+// * K and V tiles go HBM -> LDS directly (buffer_load_dwordx4 ... lds), 16 bytes
+//   per lane; rows past N fall outside the buffer's range and read as zero.
+//   LDS rows are XOR-swizzled at 16-byte granularity (the swizzle is applied to
+//   the global address, since the direct loads fill LDS lane-linearly).
 // * Scores are kept raw; the softmax scale and log2(e) are folded into one
 //   multiply-add before v_exp_f32, which computes 2^x natively, and the running
 //   maximum lives in log2 units of the scaled scores (the exp2 change of "How to
@@ -47,43 +52,48 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 
 template <int D, int QB, int WAVES, int BK>
 struct Tile {
   static constexpr int kThreads = WAVES * 64;
   static constexpr int kBQ = WAVES * QB * 32;
-  static constexpr int kChunksPerRow = D / 8;            // 16-byte chunks per K/V row
-  static constexpr int kKBytes = BK * D * 2;             // one K tile (bf16)
-  static constexpr int kVBytes = BK * D * 2;             // one V^T tile (bf16)
-  static constexpr int kStageBytes = kKBytes + kVBytes;
-  static constexpr int kLdsBytes = 2 * kStageBytes;      // double-buffered ring
-  static constexpr int kKChunks = BK * kChunksPerRow;    // 16-byte chunks per K tile
-  static constexpr int kVUnits = (BK / 2) * kChunksPerRow;  // (key pair, 8 dims) units
-  static constexpr int kKIters = (kKChunks + kThreads - 1) / kThreads;
-  static constexpr int kVIters = (kVUnits + kThreads - 1) / kThreads;
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTileBytes = BK * kRowBytes;       // one K or V tile (bf16)
+  static constexpr int kStageBytes = 2 * kTileBytes;      // K then V
+  static constexpr int kLdsBytes = 2 * kStageBytes;       // double-buffered ring
+  static constexpr int kBlocks = kTileBytes / 1024;       // 1 KB direct-load blocks per tile
+  static constexpr int kBlocksPerWave = (kBlocks + WAVES - 1) / WAVES;
   static_assert(D == 64 || D == 128, "head dim");
-  static_assert(BK % 32 == 0 && BK >= 64 && BK <= 128, "key tile");
+  static_assert(BK % 32 == 0 && BK >= 32 && BK <= 128, "key tile");
+  static_assert(kTileBytes % 1024 == 0, "tile = whole 1 KB blocks");
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one CU");
 };
 
-// K tile in LDS: row = key, 16-byte chunk c stored at chunk position c ^ (row & 7),
-// so the 8 lanes of one ds_read_b128 phase (8 rows, one chunk) hit 8 distinct
-// bank groups.
+// Swizzle of the 16-byte chunks of LDS row `row` (K and V tiles alike):
+// chunk c is stored at position c ^ swz(row).  For 128-byte rows (d = 64) the
+// position depends on row bits 1..3 (bit-reversed), for 256-byte rows (d = 128)
+// on row bits 0..3 (2-bit fields swapped); both keep the K fragment reads (16
+// rows, one chunk) and the V transpose reads (4 rows, 4 chunks) on distinct
+// banks.
 template <int D>
-__device__ __forceinline__ int k_lds_offset(int row, int chunk) {
-  return row * (D * 2) + ((chunk ^ (row & 7)) << 4);
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 64) {
+    const int m = (row >> 1) & 7;
+    return ((m & 1) << 2) | (m & 2) | ((m >> 2) & 1);
+  } else {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  }
 }
 
-// V^T tile in LDS: row = head-dim index, BK keys per row in 8-byte chunks of 4
-// keys; chunk c stored at position c ^ f(row) with f(row) = (row ^ (row >> 3)) & 15.
-// Reads (16 rows, one chunk) and the transposing writes (rows 8 apart) are
-// both spread across distinct banks by it.
-template <int BK>
-__device__ __forceinline__ int vt_lds_offset(int row, int key) {
-  const int f = (row ^ (row >> 3)) & 15;
-  return row * (BK * 2) + (((key >> 2) ^ f) << 3) + ((key & 3) << 1);
+template <int D>
+__device__ __forceinline__ int lds_offset(int row, int chunk) {
+  return row * (D * 2) + ((chunk ^ swz<D>(row)) << 4);
 }
 
 __device__ __forceinline__ float lane_swap_max(float x) {
@@ -102,70 +112,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-template <int D, int QB, int WAVES, int BK>
-struct Regs {
-  using T = Tile<D, QB, WAVES, BK>;
-  u32x4 k[T::kKIters];
-  u32x4 va[T::kVIters];
-  u32x4 vb[T::kVIters];
-};
-
-// Global -> registers for key tile starting at k0 (rows >= N are zero-filled).
-template <int D, int QB, int WAVES, int BK>
-__device__ __forceinline__ void load_tile(Regs<D, QB, WAVES, BK>& r, const uint16_t* __restrict__ kh,
-                                          const uint16_t* __restrict__ vh, int k0, int N, int tid) {
-  using T = Tile<D, QB, WAVES, BK>;
-#pragma unroll
-  for (int it = 0; it < T::kKIters; ++it) {
-    const int u = tid + it * T::kThreads;
-    const int row = u / T::kChunksPerRow, c = u % T::kChunksPerRow;
-    const int key = k0 + row;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if ((T::kKChunks % T::kThreads == 0 || u < T::kKChunks) && key < N)
-      x = *reinterpret_cast<const u32x4*>(kh + (size_t)key * D + c * 8);
-    r.k[it] = x;
-  }
-#pragma unroll
-  for (int it = 0; it < T::kVIters; ++it) {
-    const int u = tid + it * T::kThreads;
-    const int kp = u / T::kChunksPerRow, c = u % T::kChunksPerRow;
-    const int key = k0 + 2 * kp;
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    const bool live = (T::kVUnits % T::kThreads == 0 || u < T::kVUnits);
-    if (live && key < N) a = *reinterpret_cast<const u32x4*>(vh + (size_t)key * D + c * 8);
-    if (live && key + 1 < N) b = *reinterpret_cast<const u32x4*>(vh + (size_t)(key + 1) * D + c * 8);
-    r.va[it] = a;
-    r.vb[it] = b;
-  }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
 }
 
-// Registers -> LDS stage: K as is (swizzled), V transposed into V^T.
-template <int D, int QB, int WAVES, int BK>
-__device__ __forceinline__ void store_tile(const Regs<D, QB, WAVES, BK>& r, char* stage, int tid) {
-  using T = Tile<D, QB, WAVES, BK>;
-#pragma unroll
-  for (int it = 0; it < T::kKIters; ++it) {
-    const int u = tid + it * T::kThreads;
-    if (T::kKChunks % T::kThreads == 0 || u < T::kKChunks) {
-      const int row = u / T::kChunksPerRow, c = u % T::kChunksPerRow;
-      *reinterpret_cast<u32x4*>(stage + k_lds_offset<D>(row, c)) = r.k[it];
-    }
-  }
-  char* vt = stage + T::kKBytes;
-#pragma unroll
-  for (int it = 0; it < T::kVIters; ++it) {
-    const int u = tid + it * T::kThreads;
-    if (T::kVUnits % T::kThreads == 0 || u < T::kVUnits) {
-      const int kp = u / T::kChunksPerRow, c = u % T::kChunksPerRow;
-      const int key = 2 * kp;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t a = r.va[it][e >> 1], b = r.vb[it][e >> 1];
-        const uint32_t w = (e & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
-        *reinterpret_cast<uint32_t*>(vt + vt_lds_offset<BK>(c * 8 + e, key)) = w;
-      }
-    }
-  }
+// 16 bytes per lane, global -> LDS: lane l's bytes land at dst + 16*l (dst is
+// wave-uniform).  Kept out of the kernel template: called directly from a
+// template body, this builtin stops the host pass from emitting launch stubs.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* dst, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, voffset, 0, 0, 0);
 }
 
 template <int D, bool CAUSAL, int QB, int WAVES, int BK>
@@ -173,7 +128,11 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ out, float* __restrict__ lse, int BH, int N, int nqt, float qk_scale) {
   using T = Tile<D, QB, WAVES, BK>;
-  __shared__ __attribute__((aligned(16))) char lds[T::kLdsBytes];
+  // One array per ring stage: distinct objects let the compiler see that the
+  // direct loads into one stage never alias the fragment reads of the other,
+  // so it does not wait for the prefetch before reading the current tile.
+  __shared__ __attribute__((aligned(1024))) char lds0[T::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds1[T::kStageBytes];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -183,9 +142,9 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(
 
   // ---- which (head, query tile) this workgroup owns -------------------------
   // Workgroups are dispatched round-robin over the 8 XCDs; when the head count
-  // allows, the ids are remapped so that each XCD works through a contiguous
-  // set of heads (their K/V stay in that XCD's L2).  Causal tiles run longest
-  // first, all heads' longest tiles before any shorter one.
+  // allows, ids are remapped so that each XCD works through a contiguous set of
+  // heads (their K/V stay in that XCD's L2).  Causal tiles run longest first,
+  // all heads' longest tiles before any shorter one.
   const int total = gridDim.x;
   const int i = blockIdx.x;
   const bool xcd = (BH % 8) == 0;
@@ -207,23 +166,55 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(
   }
 
   const size_t head = (size_t)bh * N * D;
-  const uint16_t* qh = q + head;
-  const uint16_t* kh = k + head;
-  const uint16_t* vh = v + head;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + head, head_bytes);
   const int q0 = qt * T::kBQ;
   const int qw = q0 + wave * (QB * 32);  // first query of this wavefront
 
-  // ---- Q block -> VGPRs, as the B operand of S^T = K Q^T ---------------------
+  // ---- Q block -> VGPRs, as the B operand of S^T = K Q^T (rows >= N read 0) ----
   bf16x8 qreg[QB][D / 16];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qw + qb * 32 + lr;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < N) x = *reinterpret_cast<const u32x4*>(qh + (size_t)row * D + ks * 16 + g * 8);
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(qrs, (row * D + ks * 16 + g * 8) * 2, 0, 0);
       qreg[qb][ks] = __builtin_bit_cast(bf16x8, x);
     }
+  }
+
+  // ---- per-lane LDS offsets (loop invariant) ---------------------------------
+  // Direct loads: this wave fills 1 KB blocks b = wave + WAVES*n of each tile;
+  // lane l lands at byte 1024*b + 16*l, i.e. at LDS (row, position) and must
+  // fetch global chunk position ^ swz(row) of that row.
+  uint32_t dma_src[T::kBlocksPerWave];
+#pragma unroll
+  for (int n = 0; n < T::kBlocksPerWave; ++n) {
+    const int p = (wave + WAVES * n) * 64 + lane;  // 16-byte slot in the tile
+    const int row = p / (D / 8), pos = p % (D / 8);
+    dma_src[n] = row * (D * 2) + ((pos ^ swz<D>(row)) << 4);
+  }
+  // K fragment reads: key row kb*32 + lr, chunk 2*ks + g.
+  int koff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = lds_offset<D>(lr, 2 * ks + g);
+  // V transpose reads: in each 16-lane group (s = lane / 16), lane 4r + tt
+  // supplies 4 elements of key row (kbase + r) starting at column 4*tt of the
+  // group's 16 columns; the group's columns are db*32 + 16*(s & 1) + 0..15 and
+  // kbase = kb*32 + 16*h + 4*g (+8 for the upper half of the 8 k-slots).
+  int voff[D / 32][2];
+  {
+    const int s = lane >> 4, jj = lane & 15, r = jj >> 2, tt = jj & 3;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int key = 4 * g + r + 8 * hi;
+        const int col = db * 32 + 16 * (s & 1) + 4 * tt;
+        voff[db][hi] = lds_offset<D>(key, col >> 3) + ((col & 4) << 1);
+      }
   }
 
   f32x16 oacc[QB][D / 32];
@@ -240,109 +231,133 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(
   const int kend = CAUSAL ? min(q0 + T::kBQ, N) : N;
   const int ntiles = (kend + BK - 1) / BK;
 
-  Regs<D, QB, WAVES, BK> regs;
-  load_tile<D, QB, WAVES, BK>(regs, kh, vh, 0, N, tid);
-  store_tile<D, QB, WAVES, BK>(regs, lds, tid);
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    char* stage = lds + (j & 1) * T::kStageBytes;
-    const int k0 = j * BK;
-    const bool more = j + 1 < ntiles;
-    if (more) load_tile<D, QB, WAVES, BK>(regs, kh, vh, k0 + BK, N, tid);
-
-    // Wave-uniform classification of this key tile for this wavefront.
-    const bool skip = CAUSAL && (k0 > qw + QB * 32 - 1);
-    const bool masked = (CAUSAL && (k0 + BK - 1 > qw)) || (k0 + BK > N);
-    if (!skip) {
-      // ---- S^T = K_j Q^T --------------------------------------------------
-      f32x16 s[QB][BK / 32];
+  auto issue_tile = [&](int j, int stage) {
+    const uint32_t gbase = (uint32_t)j * BK * (D * 2);
 #pragma unroll
-      for (int kb = 0; kb < BK / 32; ++kb) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + k_lds_offset<D>(kb * 32 + lr, 2 * ks + g));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][ks], s[qb][kb], 0, 0, 0);
-        }
+    for (int n = 0; n < T::kBlocksPerWave; ++n) {
+      const int b = wave + WAVES * n;
+      if (T::kBlocks % WAVES == 0 || b < T::kBlocks) {
+        char* kdst = (stage ? lds1 : lds0) + b * 1024;
+        // The whole offset goes in the VGPR operand so the range check sees it.
+        dma16(krs, kdst, dma_src[n] + gbase);
+        dma16(vrs, kdst + T::kTileBytes, dma_src[n] + gbase);
       }
+    }
+  };
 
-      // ---- mask, online softmax, P -> bf16 ---------------------------------
-      bf16x8 p[QB][BK / 16];
+  auto compute_tile = [&](const char* kst, int k0, bool masked) {
+    const char* vst = kst + T::kTileBytes;
+    // ---- S^T = K_j Q^T ------------------------------------------------------
+    f32x16 s[QB][BK / 32];
+#pragma unroll
+    for (int kb = 0; kb < BK / 32; ++kb) {
+      bf16x8 a[D / 16];
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        a[ks] = *reinterpret_cast<const bf16x8*>(kst + kb * 32 * (D * 2) + koff[ks]);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        if (masked) {
-          const int query = qw + qb * 32 + lr;
+        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], qreg[qb][0], f32x16{}, 0, 0, 0);
 #pragma unroll
-          for (int kb = 0; kb < BK / 32; ++kb)
+        for (int ks = 1; ks < D / 16; ++ks)
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qreg[qb][ks], s[qb][kb], 0, 0, 0);
+      }
+    }
+    // ---- V fragments (issued early; consumed after the softmax) --------------
+    bf16x8 va[D / 32][BK / 16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-              if ((CAUSAL && key > query) || key >= N) s[qb][kb][r] = -__builtin_inff();
-            }
-        }
-        float mx = s[qb][0][0];
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int kb = 0; kb < BK / 32; ++kb)
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int rowoff = kk * 16 * (D * 2);  // keys kk*16 .. (kb = kk/2, h = kk%2)
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vst + rowoff + voff[db][0]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vst + rowoff + voff[db][1]));
+        const u32x4 w = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                         __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+        va[db][kk] = __builtin_bit_cast(bf16x8, w);
+      }
+    // ---- mask, online softmax, P -> bf16 -------------------------------------
+    bf16x8 p[QB][BK / 16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-        mx = lane_swap_max(mx);
-        const float m_new = fmaxf(m[qb], mx * qk_scale);
-        // A row that has seen no visible key yet keeps m = -inf; subtract 0 then
-        // so that exp2(-inf - (-inf)) never appears.
-        const float m_sub = (m_new == -__builtin_inff()) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m[qb] - m_sub);
-        m[qb] = m_new;
-        float rs = 0.f;
+    for (int qb = 0; qb < QB; ++qb) {
+      if (masked) {
+        const int query = qw + qb * 32 + lr;
 #pragma unroll
         for (int kb = 0; kb < BK / 32; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r], qk_scale, -m_sub));
-            s[qb][kb][r] = e;
-            rs += e;
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if ((CAUSAL && key > query) || key >= N) s[qb][kb][r] = -__builtin_inff();
           }
-        l[qb] = fmaf(alpha, l[qb], rs);
+      }
+      float mx = fmaxf(s[qb][0][0], s[qb][0][1]);
+#pragma unroll
+      for (int kb = 0; kb < BK / 32; ++kb)
+#pragma unroll
+        for (int r = (kb == 0 ? 2 : 0); r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+      mx = lane_swap_max(mx);
+      const float m_new = fmaxf(m[qb], mx * qk_scale);
+      // A row that has seen no visible key yet keeps m = -inf; subtract 0 then
+      // so that exp2(-inf - (-inf)) never appears.
+      const float m_sub = (m_new == -__builtin_inff()) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m[qb] - m_sub);
+      m[qb] = m_new;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < BK / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r], qk_scale, -m_sub));
+          s[qb][kb][r] = e;
+          rs += e;
+        }
+      l[qb] = fmaf(alpha, l[qb], rs);
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha;
-#pragma unroll
-        for (int kb = 0; kb < BK / 32; ++kb)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            u32x4 w;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[qb][kb][8 * h + 2 * e], s[qb][kb][8 * h + 2 * e + 1]);
-            p[qb][2 * kb + h] = __builtin_bit_cast(bf16x8, w);
-          }
       }
-
-      // ---- O^T += V_j^T P^T ------------------------------------------------
-      const char* vt = stage + T::kKBytes;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int row = db * 32 + lr;
+      for (int kb = 0; kb < BK / 32; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < BK / 32; ++kb)
+        for (int h = 0; h < 2; ++h) {
+          u32x4 w;
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int key = kb * 32 + 16 * h + 4 * g;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vt + vt_lds_offset<BK>(row, key));
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + vt_lds_offset<BK>(row, key + 8));
-            const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-            const bf16x8 a = __builtin_bit_cast(bf16x8, w);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-              oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[qb][2 * kb + h], oacc[qb][db], 0, 0, 0);
-          }
-      }
+          for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[qb][kb][8 * h + 2 * e], s[qb][kb][8 * h + 2 * e + 1]);
+          p[qb][2 * kb + h] = __builtin_bit_cast(bf16x8, w);
+        }
     }
+    // ---- O^T += V_j^T P^T ------------------------------------------------------
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][kk], p[qb][kk], oacc[qb][db], 0, 0, 0);
+  };
 
-    if (more) store_tile<D, QB, WAVES, BK>(regs, lds + ((j + 1) & 1) * T::kStageBytes, tid);
+  auto step = [&](int j, int stage) {
+    if (j + 1 < ntiles) issue_tile(j + 1, stage ^ 1);
+    const int k0 = j * BK;
+    // Wave-uniform classification of this key tile for this wavefront.
+    const bool skip = CAUSAL && (k0 > qw + QB * 32 - 1);
+    const bool masked = (CAUSAL && (k0 + BK - 1 > qw)) || (k0 + BK > N);
+    if (!skip) compute_tile(stage ? lds1 : lds0, k0, masked);
+    // This wave's direct loads into the other stage have landed; after the
+    // barrier every wave's have, and every wave is done reading this stage.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
+  };
+
+  issue_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  int j = 0;
+  for (; j + 1 < ntiles; j += 2) {
+    step(j, 0);
+    step(j + 1, 1);
   }
+  if (j < ntiles) step(j, 0);
 
   // ---- epilogue: O / l -> bf16, LSE = (m + log2 l) ln 2 ------------------------
 #pragma unroll

@@ -95,3 +95,10 @@ def test_no_device_on_cpu_host(lib):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert call() == 8
+
+
+def test_no_undefined_kernel_launch_stubs():
+    """Every kernel variant's host launch stub is defined in the library (a
+    template body the host pass cannot instantiate leaves it undefined)."""
+    out = os.popen("nm -D %s" % fa.LIB).read()
+    assert not re.findall(r"\bU \S*device_stub\S*", out)
