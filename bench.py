@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -51,7 +52,26 @@ def parse():
     ap.add_argument("--cfg", type=str, default=None, help="force a tile variant: qb,waves,bk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows-per-head", type=int, default=None)
+    ap.add_argument("--ramp-seconds", type=float, default=1.0,
+                    help="extra back-to-back launches before timing, so clocks ramp up")
+    ap.add_argument("--only", choices=["noncausal", "causal"], default=None,
+                    help="run one mode only (counter collection)")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="instead of attention, run a plain device copy of MIB MiB (calibrates byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int, reps: int = 5):
+    """A plain device-to-device copy of known size, for scaling HBM byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": True, "bytes_read_per_copy": n * 4, "bytes_written_per_copy": n * 4,
+                      "copies": reps}), flush=True)
 
 
 def main():
@@ -63,6 +83,10 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calib:
+        copy_calibration(args.copy_calib)
+        return
+
     import torch
     import flashattention_forward_fa2_amd as fa
     import inputs
@@ -73,6 +97,11 @@ def main():
     w = inputs.WORKLOADS[args.workload]
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
     modes = list(w["modes"]) if args.workload != 3 else [0, 1]
+    if args.only:
+        modes = [c for c in modes if c == (args.only == "causal")]
+        if not modes:
+            print("workload %d has no %s mode" % (args.workload, args.only), file=sys.stderr)
+            sys.exit(2)
     scale = inputs.default_scale(d)
     cfg = tuple(int(x) for x in args.cfg.split(",")) if args.cfg else None
 
@@ -93,7 +122,7 @@ def main():
         for c in modes:
             launch(c)
     torch.cuda.synchronize()
-    t_end = time.time() + 1.0
+    t_end = time.time() + args.ramp_seconds
     while time.time() < t_end:
         for c in modes:
             launch(c)
@@ -129,7 +158,7 @@ def main():
     dom_c = max(modes, key=lambda c: per_mode["causal" if c else "noncausal"]["kernel_ms_avg"])
     dom = per_mode["causal" if dom_c else "noncausal"]
     roofline = dict(bound="mfma", achieved=dom["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=dom["frac_of_peak"], traffic=None,
+                    frac=dom["frac_of_peak"], traffic=measured_traffic(B, H, N, d, dom_c),
                     kernel="fa_fwd_kernel d=%d causal=%d cfg=%s" % (d, dom_c, dom["cfg"]),
                     flops_per_launch=flops(B, H, N, d, dom_c))
 
@@ -141,7 +170,7 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(value / PAGES_STEP_TFLOPS, 3) if args.workload == 3 else None,
+        "vs_baseline": round(value / PAGES_STEP_TFLOPS, 3) if args.workload == 3 and len(modes) == 2 else None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "%s %s" % (w["name"], "+".join("causal" if c else "non-causal" for c in modes)),
                    "B": B, "H": H, "N": N, "d": d, "scale": scale, "sigma_qk": w["sigma_qk"],
@@ -152,6 +181,23 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
+def measured_traffic(B, H, N, d, causal):
+    """HBM bytes per launch from the committed counter summary under profiles/
+    (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's counts), or None when
+    there is none for this shape or the kernel sources changed since."""
+    from flashattention_forward_fa2_amd.buildlib import source_digest
+    path = os.path.join(ROOT, "profiles", "fa_fwd_d%d_B%dH%dN%d_hbm_traffic.md" % (d, B, H, N))
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    digest = re.search(r"kernel-source-sha256: ([0-9a-f]{64})", text)
+    if not digest or digest.group(1) != source_digest():
+        return None
+    m = re.search(r"traffic-bytes-per-launch d%d %s B%dH%dN%d: (\d+)"
+                  % (d, "causal" if causal else "noncausal", B, H, N), text)
+    return int(m.group(1)) if m else None
+
+
 def cpu_baseline(args, w, modes, q_bits, k_bits, v_bits, scale, outs, lses):
     """The oracle, as it stands, on a bounded row sample of the same workload."""
     import torch
@@ -159,10 +205,13 @@ def cpu_baseline(args, w, modes, q_bits, k_bits, v_bits, scale, outs, lses):
     from inputs import bf16_bits_to_f64, sample_rows, workload_seed
 
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
-    # About 16 GFLOP of fp64 oracle work (seconds on a many-core host).
+    # About 200 GFLOP of fp64 oracle work (~10 s on 16 host cores), at most every row.
     mode_weight = sum(0.5 if c else 1.0 for c in modes)
-    per_head = args.cpu_rows_per_head or int(np.clip(16e9 / (B * H * 4.0 * N * d * mode_weight), 16, N))
-    rows = sample_rows(workload_seed(args.workload, 3), B, H, N, per_head=per_head)
+    per_head = args.cpu_rows_per_head or int(np.clip(200e9 / (B * H * 4.0 * N * d * mode_weight), 16, N))
+    if per_head >= N:  # the budget covers the whole workload: every row
+        rows = np.arange(B * H * N, dtype=np.int64)
+    else:
+        rows = sample_rows(workload_seed(args.workload, 3), B, H, N, per_head=per_head)
     i = rows % N
     total_flops, total_s = 0.0, 0.0
     parity = {}
@@ -189,7 +238,7 @@ def cpu_baseline(args, w, modes, q_bits, k_bits, v_bits, scale, outs, lses):
         pass
     return dict(value=round(total_flops / total_s / 1e12, 6), unit="TFLOP/s", cores=oracle.num_threads(),
                 kind="oracle",
-                sample="%d rows (%d per head, fixed edge rows + seeded) of %s, modes %s; fp64, %.1f GFLOP in %.2fs"
+                sample="%d rows (%d per head; all rows, or fixed edge rows + seeded) of %s, modes %s; fp64, %.1f GFLOP in %.2fs"
                        % (rows.size, per_head, w["name"], modes, total_flops / 1e9, total_s),
                 cpu_model=cpu_model, parity_on_sample=parity)
 

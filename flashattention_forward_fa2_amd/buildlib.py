@@ -1,6 +1,7 @@
 """Build libfa_fwd.so (HIP, gfx950 only) in-tree with hipcc."""
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -17,6 +18,17 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 # MFMA accumulators in VGPRs: no AGPR<->VGPR copies around the rescale
                 "-mllvm", "-amdgpu-mfma-vgpr-form"]
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources and device flags: identifies the compiled
+    kernel, so that measurements taken on one build are not reported for another."""
+    h = hashlib.sha256()
+    for name in ("fa_fwd_kernel.hpp", "fa_fwd.hip"):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    h.update(" ".join(DEVICE_FLAGS).encode())
+    return h.hexdigest()
 
 
 def build(verbose: bool = False, extra=()) -> str:
