@@ -56,6 +56,8 @@ def parse():
                     help="extra back-to-back launches before timing, so clocks ramp up")
     ap.add_argument("--only", choices=["noncausal", "causal"], default=None,
                     help="run one mode only (counter collection)")
+    ap.add_argument("--layout", choices=["bhnd", "bnhd"], default="bhnd",
+                    help="bnhd: q, k, v, out stored [B, N, H, d] and passed as strided views (fa_fwd_ex)")
     ap.add_argument("--flush-reps", type=int, default=10,
                     help="launches per mode timed again with caches flushed before each (0: skip)")
     ap.add_argument("--no-gemm", action="store_true", help="skip the attainable-GEMM reference")
@@ -113,12 +115,20 @@ def main():
     print("[bench] inputs %s generated in %.1fs" % (w["name"], time.time() - t0), file=sys.stderr, flush=True)
     to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
     q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
-    outs = {c: torch.empty_like(q) for c in modes}
+    if args.layout == "bnhd":
+        # stored [B, N, H, d]; the kernel sees [B, H, N, d] views with row stride H*d
+        q, k, v = (t.permute(0, 2, 1, 3).contiguous().transpose(1, 2) for t in (q, k, v))
+        outs = {c: torch.empty((B, N, H, d), dtype=torch.bfloat16, device=dev).transpose(1, 2) for c in modes}
+    else:
+        outs = {c: torch.empty_like(q) for c in modes}
     lses = {c: torch.empty((B, H, N), dtype=torch.float32, device=dev) for c in modes}
     stream = torch.cuda.current_stream(dev)
 
     def launch(c):
-        fa.fa_fwd(q, k, v, scale=scale, causal=bool(c), out=outs[c], lse=lses[c], stream=stream, cfg=cfg)
+        if args.layout == "bnhd":
+            fa.fa_fwd_ex(q, k, v, scale=scale, causal=bool(c), out=outs[c], lse=lses[c], stream=stream, cfg=cfg)
+        else:
+            fa.fa_fwd(q, k, v, scale=scale, causal=bool(c), out=outs[c], lse=lses[c], stream=stream, cfg=cfg)
 
     # Warm-up: the requested steps, then keep the GPU busy ~1 s so clocks ramp.
     for _ in range(max(1, args.warmup)):
@@ -178,7 +188,8 @@ def main():
     dom_c = max(modes, key=lambda c: per_mode["causal" if c else "noncausal"]["kernel_ms_avg"])
     dom = per_mode["causal" if dom_c else "noncausal"]
     roofline = dict(bound="mfma", achieved=dom["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=dom["frac_of_peak"], traffic=measured_traffic(B, H, N, d, dom_c),
+                    frac=dom["frac_of_peak"],
+                    traffic=measured_traffic(B, H, N, d, dom_c) if args.layout == "bhnd" else None,
                     kernel="fa_fwd_kernel d=%d causal=%d cfg=%s" % (d, dom_c, dom["cfg"]),
                     flops_per_launch=flops(B, H, N, d, dom_c))
     if not args.no_gemm:
@@ -196,7 +207,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": round(value / PAGES_STEP_TFLOPS, 3) if args.workload == 3 and len(modes) == 2 else None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "%s %s" % (w["name"], "+".join("causal" if c else "non-causal" for c in modes)),
+        "config": {"workload": "%s %s%s" % (w["name"], "+".join("causal" if c else "non-causal" for c in modes),
+                                            "" if args.layout == "bhnd" else " [B,N,H,d] strided"),
                    "B": B, "H": H, "N": N, "d": d, "scale": scale, "sigma_qk": w["sigma_qk"],
                    "flops_per_step": step_flops, "modes": per_mode},
         "roofline": roofline,
@@ -263,7 +275,7 @@ def cpu_baseline(args, w, modes, q_bits, k_bits, v_bits, scale, outs, lses):
         total_s += time.perf_counter() - t0
         nkeys = (i + 1) if c else np.full(rows.shape, N)
         total_flops += float(np.sum(4.0 * nkeys * d))
-        o = bf16_bits_to_f64(outs[c].view(torch.int16).cpu().numpy().view(np.uint16)).reshape(-1, d)[rows]
+        o = bf16_bits_to_f64(outs[c].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)).reshape(-1, d)[rows]
         L = lses[c].cpu().numpy().reshape(-1)[rows]
         err = np.abs(o - o_ref)
         parity["causal" if c else "noncausal"] = dict(

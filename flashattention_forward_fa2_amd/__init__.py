@@ -13,15 +13,15 @@ import threading
 
 from .buildlib import LIB, build  # noqa: F401
 
-__all__ = ["fa_fwd", "fa_fwd_ptr", "fa_fwd_cfg", "FaError", "strerror", "version", "default_cfg",
-           "variants", "load_library", "EXPORTED_SYMBOLS"]
+__all__ = ["fa_fwd", "fa_fwd_ptr", "fa_fwd_cfg", "fa_fwd_ex", "fa_fwd_ex_ptr", "FwdDesc", "FaError", "strerror",
+           "version", "default_cfg", "variants", "load_library", "EXPORTED_SYMBOLS"]
 
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_cfg", "fa_default_cfg", "fa_num_variants", "fa_variant",
-                    "fa_strerror", "fa_version")
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_cfg", "fa_fwd_ex", "fa_fwd_ex_cfg", "fa_default_cfg", "fa_num_variants",
+                    "fa_variant", "fa_strerror", "fa_version")
 
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD_DIM", 4: "FA_ERR_SCALE",
           5: "FA_ERR_ARG", 6: "FA_ERR_ALIGN", 7: "FA_ERR_ALIAS", 8: "FA_ERR_NO_DEVICE",
-          9: "FA_ERR_LAUNCH", 10: "FA_ERR_INTERNAL"}
+          9: "FA_ERR_LAUNCH", 10: "FA_ERR_INTERNAL", 11: "FA_ERR_STRIDE"}
 
 
 class FaError(RuntimeError):
@@ -35,6 +35,21 @@ class TileCfg(ctypes.Structure):
 
     def as_tuple(self):
         return (self.qb, self.waves, self.bk)
+
+
+_LL3 = ctypes.c_longlong * 3
+_LL2 = ctypes.c_longlong * 2
+
+
+class FwdDesc(ctypes.Structure):
+    """Mirror of ``fa_fwd_desc`` (include/fa_fwd.h): general lengths and strides."""
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("B", ctypes.c_int), ("H", ctypes.c_int), ("Nq", ctypes.c_int), ("Nk", ctypes.c_int),
+                ("d", ctypes.c_int),
+                ("q_stride", _LL3), ("k_stride", _LL3), ("v_stride", _LL3), ("o_stride", _LL3),
+                ("lse_stride", _LL2),
+                ("scale", ctypes.c_float), ("causal", ctypes.c_int), ("stream", ctypes.c_void_p)]
 
 
 _lock = threading.Lock()
@@ -57,6 +72,10 @@ def load_library():
             lib.fa_fwd.restype = _I
             lib.fa_fwd_cfg.argtypes = fwd_args + [ctypes.POINTER(TileCfg)]
             lib.fa_fwd_cfg.restype = _I
+            lib.fa_fwd_ex.argtypes = [ctypes.POINTER(FwdDesc)]
+            lib.fa_fwd_ex.restype = _I
+            lib.fa_fwd_ex_cfg.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(TileCfg)]
+            lib.fa_fwd_ex_cfg.restype = _I
             lib.fa_default_cfg.argtypes = [_I, _I, _I, ctypes.POINTER(TileCfg)]
             lib.fa_default_cfg.restype = _I
             lib.fa_num_variants.argtypes = []
@@ -155,3 +174,59 @@ def fa_fwd_cfg(q, k, v, cfg, scale: float | None = None, causal: bool = False, o
                stream=None):
     """``fa_fwd`` with an explicit ``(qb, waves, bk)`` tile configuration."""
     return fa_fwd(q, k, v, scale=scale, causal=causal, out=out, lse=lse, stream=stream, cfg=tuple(cfg))
+
+
+def fa_fwd_ex_ptr(desc: FwdDesc, cfg=None) -> int:
+    """Raw descriptor call; returns the library's status code (does not raise)."""
+    lib = load_library()
+    if cfg is None:
+        return int(lib.fa_fwd_ex(ctypes.byref(desc)))
+    c = TileCfg(*cfg)
+    return int(lib.fa_fwd_ex_cfg(ctypes.byref(desc), ctypes.byref(c)))
+
+
+def fa_fwd_ex(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse=None,
+              stream=None, cfg=None):
+    """Attention forward on strided torch bf16 views, N_q queries over N_k keys.
+
+    ``q`` is [B, H, Nq, d] and ``k``, ``v`` are [B, H, Nk, d], each with any
+    strides whose last one is 1 (a [B, N, H, d] tensor is passed as
+    ``t.transpose(1, 2)``).  Causal masking is top-left: key j is visible to
+    query i iff j <= i.  ``out`` (default: a new contiguous tensor) is a
+    [B, H, Nq, d] bf16 view, ``lse`` a [B, H, Nq] fp32 view with unit row stride.
+    Returns ``(out, lse)``; enqueued on ``stream`` (default: the current stream).
+    """
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, H, Nq, d], k and v one [B, H, Nk, d] shape")
+    B, H, Nq, d = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
+        raise ValueError("q, k, v must agree on B, H and d")
+    Nk = k.shape[2]
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or t.stride(3) != 1:
+            raise ValueError("q, k, v must be bfloat16 device views with a contiguous last dimension")
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if out.shape != (B, H, Nq, d) or out.dtype != torch.bfloat16 or out.stride(3) != 1:
+        raise ValueError("out must be a bf16 [B, H, Nq, d] view with a contiguous last dimension")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or lse.stride(2) != 1:
+        raise ValueError("lse must be an fp32 [B, H, Nq] view with unit row stride")
+    desc = FwdDesc()
+    desc.q, desc.k, desc.v, desc.out, desc.lse = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                                   lse.data_ptr())
+    desc.B, desc.H, desc.Nq, desc.Nk, desc.d = B, H, Nq, Nk, d
+    desc.q_stride = _LL3(*q.stride()[:3])
+    desc.k_stride = _LL3(*k.stride()[:3])
+    desc.v_stride = _LL3(*v.stride()[:3])
+    desc.o_stride = _LL3(*out.stride()[:3])
+    desc.lse_stride = _LL2(*lse.stride()[:2])
+    desc.scale = float(scale)
+    desc.causal = int(bool(causal))
+    desc.stream = _stream_handle(stream, q.device)
+    _check(fa_fwd_ex_ptr(desc, None if cfg is None else tuple(cfg)))
+    return out, lse

@@ -8,38 +8,38 @@
 #include <cstdint>
 #include <cstring>
 #include <mutex>
+#include <utility>
 
 #include "fa_fwd_kernel.hpp"
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 
-using Launcher = hipError_t (*)(const void*, const void*, const void*, void*, float*, int BH, int N,
-                                float qk_scale, hipStream_t);
+using Launcher = hipError_t (*)(const fa::Params&, int B, hipStream_t);
 
 struct Variant {
   int d, causal, qb, waves, bk;
-  Launcher launch;
+  Launcher launch;          // contiguous [B, H, N, d] tensors
+  Launcher launch_strided;  // any strides
 };
 
-template <int D, bool CAUSAL, int QB, int WAVES, int BK>
-hipError_t launch_variant(const void* q, const void* k, const void* v, void* out, float* lse, int BH,
-                          int N, float qk_scale, hipStream_t stream) {
+template <int D, bool CAUSAL, int QB, int WAVES, int BK, bool STRIDED>
+hipError_t launch_variant(const fa::Params& p, int B, hipStream_t stream) {
   using T = fa::Tile<D, QB, WAVES, BK>;
-  const int nqt = (N + T::kBQ - 1) / T::kBQ;
-  const long long blocks = (long long)BH * nqt;
+  fa::Params pr = p;
+  pr.nqt = (p.Nq + T::kBQ - 1) / T::kBQ;
+  const long long blocks = (long long)B * p.H * pr.nqt;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fa::fa_fwd_kernel<D, CAUSAL, QB, WAVES, BK>), dim3((unsigned)blocks),
-                     dim3(T::kThreads), 0, stream, static_cast<const uint16_t*>(q),
-                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                     static_cast<uint16_t*>(out), lse, BH, N, nqt, qk_scale);
+  hipLaunchKernelGGL((fa::fa_fwd_kernel<D, CAUSAL, QB, WAVES, BK, STRIDED>), dim3((unsigned)blocks), dim3(T::kThreads), 0,
+                     stream, pr);
   return hipGetLastError();
 }
 
-#define FA_VARIANT(D, C, QB, W, BK) {D, C, QB, W, BK, &launch_variant<D, (C) != 0, QB, W, BK>}
+#define FA_VARIANT(D, C, QB, W, BK) \
+  {D, C, QB, W, BK, &launch_variant<D, (C) != 0, QB, W, BK, false>, &launch_variant<D, (C) != 0, QB, W, BK, true>}
 #define FA_VARIANTS_DC(D, C) \
-  FA_VARIANT(D, C, 1, 4, 64), FA_VARIANT(D, C, 2, 4, 64), FA_VARIANT(D, C, 1, 8, 64), FA_VARIANT(D, C, 2, 4, 128)
+  FA_VARIANT(D, C, 1, 4, 64), FA_VARIANT(D, C, 2, 4, 64), FA_VARIANT(D, C, 1, 8, 64)
 
 const Variant kVariants[] = {
     FA_VARIANTS_DC(64, 0), FA_VARIANTS_DC(64, 1), FA_VARIANTS_DC(128, 0), FA_VARIANTS_DC(128, 1),
@@ -66,7 +66,7 @@ int validate(const void* q, const void* k, const void* v, const void* out, const
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
   const long long elems = (long long)B * H * N * d;
-  if ((long long)N * d >= (1LL << 31) || elems >= (1LL << 31)) return FA_ERR_SHAPE;
+  if ((long long)(N + 256) * d >= (1LL << 30) || elems >= (1LL << 31)) return FA_ERR_SHAPE;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
@@ -93,19 +93,97 @@ int check_device() {
   return g_dev_ok[dev] ? FA_OK : FA_ERR_NO_DEVICE;
 }
 
+// Byte extent of a strided [B, H, N, d] tensor: from its base to one past its
+// last element.
+long long extent_bytes(const long long st[3], int B, int H, int N, int d, int elem) {
+  return ((long long)(B - 1) * st[0] + (long long)(H - 1) * st[1] + (long long)(N - 1) * st[2] + d) * elem;
+}
+
+bool strides_ok(const long long st[3], int N, int d) {
+  for (int i = 0; i < 3; ++i)
+    if (st[i] < 0 || (st[i] & 7) != 0 || st[i] > (1LL << 40)) return false;
+  return st[2] >= d && (long long)(N + 256) * st[2] < (1LL << 30);
+}
+
+// Host-only checks of a descriptor, in a fixed order; no HIP call is made here.
+int validate_desc(const fa_fwd_desc& a) {
+  if (!a.q || !a.k || !a.v || !a.out || !a.lse) return FA_ERR_NULL;
+  if (a.B < 1 || a.H < 1 || a.Nq < 1 || a.Nk < 1) return FA_ERR_SHAPE;
+  if (a.d != 64 && a.d != 128) return FA_ERR_HEAD_DIM;
+  if ((long long)a.B * a.H > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (!strides_ok(a.q_stride, a.Nq, a.d) || !strides_ok(a.k_stride, a.Nk, a.d) ||
+      !strides_ok(a.v_stride, a.Nk, a.d) || !strides_ok(a.o_stride, a.Nq, a.d))
+    return FA_ERR_STRIDE;
+  if (a.lse_stride[0] < 0 || a.lse_stride[1] < 0 || a.lse_stride[0] > (1LL << 40) || a.lse_stride[1] > (1LL << 40))
+    return FA_ERR_STRIDE;
+  if (!std::isfinite(a.scale) || !(a.scale > 0.f)) return FA_ERR_SCALE;
+  if (a.causal != 0 && a.causal != 1) return FA_ERR_ARG;
+  auto al = [](const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; };
+  if (!al(a.q, 16) || !al(a.k, 16) || !al(a.v, 16) || !al(a.out, 16) || !al(a.lse, 4)) return FA_ERR_ALIGN;
+  const long long qb = extent_bytes(a.q_stride, a.B, a.H, a.Nq, a.d, 2);
+  const long long kb = extent_bytes(a.k_stride, a.B, a.H, a.Nk, a.d, 2);
+  const long long vb = extent_bytes(a.v_stride, a.B, a.H, a.Nk, a.d, 2);
+  const long long ob = extent_bytes(a.o_stride, a.B, a.H, a.Nq, a.d, 2);
+  const long long lst[3] = {a.lse_stride[0], a.lse_stride[1], 1};
+  const long long lb = extent_bytes(lst, a.B, a.H, a.Nq, 1, 4);
+  const std::pair<const void*, long long> ins[3] = {{a.q, qb}, {a.k, kb}, {a.v, vb}};
+  for (const auto& in : ins)
+    if (overlaps(a.out, (size_t)ob, in.first, (size_t)in.second) || overlaps(a.lse, (size_t)lb, in.first, (size_t)in.second))
+      return FA_ERR_ALIAS;
+  if (overlaps(a.out, (size_t)ob, a.lse, (size_t)lb)) return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
+int run_desc(const fa_fwd_desc& a, const fa_tile_cfg& cfg) {
+  const int st = validate_desc(a);
+  if (st != FA_OK) return st;
+  const Variant* var = find_variant(a.d, a.causal, cfg);
+  if (!var) return FA_ERR_ARG;
+  const int dst = check_device();
+  if (dst != FA_OK) return dst;
+  fa::Params p{};
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.out = static_cast<uint16_t*>(a.out);
+  p.lse = a.lse;
+  p.q_sb = a.q_stride[0], p.q_sh = a.q_stride[1], p.q_rs = (int)a.q_stride[2];
+  p.k_sb = a.k_stride[0], p.k_sh = a.k_stride[1], p.k_rs = (int)a.k_stride[2];
+  p.v_sb = a.v_stride[0], p.v_sh = a.v_stride[1], p.v_rs = (int)a.v_stride[2];
+  p.o_sb = a.o_stride[0], p.o_sh = a.o_stride[1], p.o_rs = (int)a.o_stride[2];
+  p.l_sb = a.lse_stride[0], p.l_sh = a.lse_stride[1];
+  p.H = a.H, p.BH = a.B * a.H, p.Nq = a.Nq, p.Nk = a.Nk;
+  // Scores are kept raw; exp(scale*s - m) = 2^(s*scale*log2(e) - m') with m' in
+  // log2 units, so the scale and log2(e) fold into one constant.
+  p.qk_scale = (float)((double)a.scale * 1.4426950408889634);
+  auto contiguous = [&](const long long st[3], int n) {
+    return st[0] == (long long)a.H * n * a.d && st[1] == (long long)n * a.d && st[2] == a.d;
+  };
+  const bool dense = contiguous(a.q_stride, a.Nq) && contiguous(a.k_stride, a.Nk) && contiguous(a.v_stride, a.Nk) &&
+                     contiguous(a.o_stride, a.Nq) && a.lse_stride[0] == (long long)a.H * a.Nq &&
+                     a.lse_stride[1] == a.Nq;
+  const hipError_t e = (dense ? var->launch : var->launch_strided)(p, a.B, static_cast<hipStream_t>(a.stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// The square, contiguous call as a descriptor.
+fa_fwd_desc square_desc(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int N,
+                        int d, float scale, int causal, void* stream) {
+  fa_fwd_desc a{};
+  a.q = q, a.k = k, a.v = v, a.out = out, a.lse = lse;
+  a.B = B, a.H = H, a.Nq = N, a.Nk = N, a.d = d;
+  const long long st[3] = {(long long)H * N * d, (long long)N * d, d};
+  for (int i = 0; i < 3; ++i) a.q_stride[i] = a.k_stride[i] = a.v_stride[i] = a.o_stride[i] = st[i];
+  a.lse_stride[0] = (long long)H * N, a.lse_stride[1] = N;
+  a.scale = scale, a.causal = causal, a.stream = stream;
+  return a;
+}
+
 int run(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int N, int d,
         float scale, int causal, void* stream, const fa_tile_cfg& cfg) {
   const int st = validate(q, k, v, out, lse, B, H, N, d, scale, causal);
   if (st != FA_OK) return st;
-  const Variant* var = find_variant(d, causal, cfg);
-  if (!var) return FA_ERR_ARG;
-  const int dst = check_device();
-  if (dst != FA_OK) return dst;
-  // Scores are kept raw; exp(scale*s - m) = 2^(s*scale*log2(e) - m') with m' in
-  // log2 units, so the scale and log2(e) fold into one constant.
-  const float qk_scale = (float)((double)scale * 1.4426950408889634);
-  const hipError_t e = var->launch(q, k, v, out, lse, B * H, N, qk_scale, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  return run_desc(square_desc(q, k, v, out, lse, B, H, N, d, scale, causal, stream), cfg);
 }
 
 }  // namespace
@@ -126,6 +204,25 @@ int fa_fwd_cfg(const void* q, const void* k, const void* v, void* out, float* ls
   if (!cfg) return FA_ERR_ARG;
   try {
     return run(q, k, v, out, lse, B, H, N, d, scale, causal, stream, *cfg);
+  } catch (...) {
+    return FA_ERR_INTERNAL;
+  }
+}
+
+int fa_fwd_ex(const fa_fwd_desc* desc) {
+  if (!desc) return FA_ERR_NULL;
+  try {
+    return run_desc(*desc, default_cfg(desc->Nk, desc->d, desc->causal));
+  } catch (...) {
+    return FA_ERR_INTERNAL;
+  }
+}
+
+int fa_fwd_ex_cfg(const fa_fwd_desc* desc, const fa_tile_cfg* cfg) {
+  if (!desc) return FA_ERR_NULL;
+  if (!cfg) return FA_ERR_ARG;
+  try {
+    return run_desc(*desc, *cfg);
   } catch (...) {
     return FA_ERR_INTERNAL;
   }
@@ -155,7 +252,7 @@ const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "null pointer argument";
-    case FA_ERR_SHAPE: return "B, H and N must be >= 1 and the tensors must have fewer than 2^31 elements";
+    case FA_ERR_SHAPE: return "B, H, N must be >= 1, tensors below 2^31 elements and (N + 256) * d below 2^30";
     case FA_ERR_HEAD_DIM: return "head dimension must be 64 or 128";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_ARG: return "invalid argument (causal must be 0 or 1; tile configuration not compiled in)";
@@ -164,6 +261,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_NO_DEVICE: return "no current HIP device, or it is not gfx950";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_INTERNAL: return "internal error";
+    case FA_ERR_STRIDE: return "a stride is negative, not a multiple of 8 elements, shorter than a row, or too large";
     default: return "unknown status";
   }
 }

@@ -28,7 +28,8 @@
 //   order in which the S^T accumulator holds the keys.  The alpha rescale of O
 //   is a per-lane scalar multiply, skipped when no lane's maximum moved.
 // * K and V tiles go HBM -> LDS directly (buffer_load_dwordx4 ... lds), 16 bytes
-//   per lane; rows past N fall outside the buffer's range and read as zero.
+//   per lane; rows past the last key fall outside the buffer's range and read
+//   as zero.
 //   LDS rows are XOR-swizzled at 16-byte granularity (the swizzle is applied to
 //   the global address, since the direct loads fill LDS lane-linearly).
 // * Scores are kept raw; the softmax scale and log2(e) are folded into one
@@ -123,11 +124,31 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* dst, ui
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, voffset, 0, 0, 0);
 }
 
-template <int D, bool CAUSAL, int QB, int WAVES, int BK>
-__global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int BH, int N, int nqt, float qk_scale) {
+// Kernel arguments.  Tensors are addressed by element strides (batch, head,
+// row); the head dimension is contiguous.  Row strides fit 32 bits and every
+// head's Q, K, V extent fits the 32-bit byte range of a buffer resource (the
+// host checks both).
+struct Params {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;
+  float* lse;
+  long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh, l_sb, l_sh;
+  int q_rs, k_rs, v_rs, o_rs;
+  int H, BH, Nq, Nk, nqt;
+  float qk_scale;
+};
+
+// STRIDED = false: every tensor is contiguous [B, H, N, d] (lse [B, H, Nq]) and
+// the strides in `pr` are ignored; the addressing then needs fewer registers.
+template <int D, bool CAUSAL, int QB, int WAVES, int BK, bool STRIDED>
+__global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
   using T = Tile<D, QB, WAVES, BK>;
+  const int BH = pr.BH, Nq = pr.Nq, Nk = pr.Nk, nqt = pr.nqt;
+  const float qk_scale = pr.qk_scale;
+  const int q_rs = STRIDED ? pr.q_rs : D, k_rs = STRIDED ? pr.k_rs : D;
+  const int v_rs = STRIDED ? pr.v_rs : D, o_rs = STRIDED ? pr.o_rs : D;
   // One array per ring stage: distinct objects let the compiler see that the
   // direct loads into one stage never alias the fragment reads of the other,
   // so it does not wait for the prefetch before reading the current tile.
@@ -165,22 +186,26 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(
     qt = t - bh * nqt;
   }
 
-  const size_t head = (size_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + head, head_bytes);
+  // Per-head bases.  A buffer resource ends at the head's last row, so rows at
+  // or past Nq (Nk) read as zero.
+  const int batch = bh / pr.H, hd = bh - batch * pr.H;
+  const long long q_off = STRIDED ? batch * pr.q_sb + hd * pr.q_sh : (long long)bh * Nq * D;
+  const long long k_off = STRIDED ? batch * pr.k_sb + hd * pr.k_sh : (long long)bh * Nk * D;
+  const long long v_off = STRIDED ? batch * pr.v_sb + hd * pr.v_sh : (long long)bh * Nk * D;
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(pr.q + q_off, (uint32_t)((Nq - 1) * q_rs + D) * 2);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(pr.k + k_off, (uint32_t)((Nk - 1) * k_rs + D) * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(pr.v + v_off, (uint32_t)((Nk - 1) * v_rs + D) * 2);
   const int q0 = qt * T::kBQ;
   const int qw = q0 + wave * (QB * 32);  // first query of this wavefront
 
-  // ---- Q block -> VGPRs, as the B operand of S^T = K Q^T (rows >= N read 0) ----
+  // ---- Q block -> VGPRs, as the B operand of S^T = K Q^T (rows >= Nq read 0) ----
   bf16x8 qreg[QB][D / 16];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qw + qb * 32 + lr;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(qrs, (row * D + ks * 16 + g * 8) * 2, 0, 0);
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(qrs, (row * q_rs + ks * 16 + g * 8) * 2, 0, 0);
       qreg[qb][ks] = __builtin_bit_cast(bf16x8, x);
     }
   }
@@ -189,12 +214,14 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(
   // Direct loads: this wave fills 1 KB blocks b = wave + WAVES*n of each tile;
   // lane l lands at byte 1024*b + 16*l, i.e. at LDS (row, position) and must
   // fetch global chunk position ^ swz(row) of that row.
-  uint32_t dma_src[T::kBlocksPerWave];
+  uint32_t dma_k[T::kBlocksPerWave], dma_v[T::kBlocksPerWave];
 #pragma unroll
   for (int n = 0; n < T::kBlocksPerWave; ++n) {
     const int p = (wave + WAVES * n) * 64 + lane;  // 16-byte slot in the tile
     const int row = p / (D / 8), pos = p % (D / 8);
-    dma_src[n] = row * (D * 2) + ((pos ^ swz<D>(row)) << 4);
+    const uint32_t col = (pos ^ swz<D>(row)) << 4;
+    dma_k[n] = row * k_rs * 2 + col;
+    dma_v[n] = row * v_rs * 2 + col;
   }
   // K fragment reads: key row kb*32 + lr, chunk 2*ks + g.
   int koff[D / 16];
@@ -227,20 +254,21 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(
     for (int db = 0; db < D / 32; ++db) oacc[qb][db] = f32x16{};
   }
 
-  // Causal: keys at or after min(q0 + BQ, N) are invisible to the whole tile.
-  const int kend = CAUSAL ? min(q0 + T::kBQ, N) : N;
+  // Causal (top-left: key j is visible to query i iff j <= i): keys at or
+  // after min(q0 + BQ, Nk) are invisible to the whole tile.
+  const int kend = CAUSAL ? min(q0 + T::kBQ, Nk) : Nk;
   const int ntiles = (kend + BK - 1) / BK;
 
   auto issue_tile = [&](int j, int stage) {
-    const uint32_t gbase = (uint32_t)j * BK * (D * 2);
+    const uint32_t gk = (uint32_t)(j * BK) * k_rs * 2, gv = (uint32_t)(j * BK) * v_rs * 2;
 #pragma unroll
     for (int n = 0; n < T::kBlocksPerWave; ++n) {
       const int b = wave + WAVES * n;
       if (T::kBlocks % WAVES == 0 || b < T::kBlocks) {
         char* kdst = (stage ? lds1 : lds0) + b * 1024;
         // The whole offset goes in the VGPR operand so the range check sees it.
-        dma16(krs, kdst, dma_src[n] + gbase);
-        dma16(vrs, kdst + T::kTileBytes, dma_src[n] + gbase);
+        dma16(krs, kdst, dma_k[n] + gk);
+        dma16(vrs, kdst + T::kTileBytes, dma_v[n] + gv);
       }
     }
   };
@@ -287,7 +315,7 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if ((CAUSAL && key > query) || key >= N) s[qb][kb][r] = -__builtin_inff();
+            if ((CAUSAL && key > query) || key >= Nk) s[qb][kb][r] = -__builtin_inff();
           }
       }
       float mx = fmaxf(s[qb][0][0], s[qb][0][1]);
@@ -341,7 +369,7 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(
     const int k0 = j * BK;
     // Wave-uniform classification of this key tile for this wavefront.
     const bool skip = CAUSAL && (k0 > qw + QB * 32 - 1);
-    const bool masked = (CAUSAL && (k0 + BK - 1 > qw)) || (k0 + BK > N);
+    const bool masked = (CAUSAL && (k0 + BK - 1 > qw)) || (k0 + BK > Nk);
     if (!skip) compute_tile(stage ? lds1 : lds0, k0, masked);
     // This wave's direct loads into the other stage have landed; after the
     // barrier every wave's have, and every wave is done reading this stage.
@@ -365,8 +393,9 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(
     const float lt = lane_swap_sum(l[qb]);
     const float inv = 1.0f / lt;
     const int query = qw + qb * 32 + lr;
-    if (query < N) {
-      uint16_t* orow = out + head + (size_t)query * D;
+    if (query < Nq) {
+      const long long o_off = STRIDED ? batch * pr.o_sb + hd * pr.o_sh : (long long)bh * Nq * D;
+      uint16_t* orow = pr.out + o_off + (long long)query * o_rs;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -376,7 +405,8 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(
           w[1] = pack_bf16x2(oacc[qb][db][4 * rr + 2] * inv, oacc[qb][db][4 * rr + 3] * inv);
           *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * rr + 4 * g) = w;
         }
-      if (g == 0) lse[(size_t)bh * N + query] = (m[qb] + log2f(lt)) * kLn2;
+      const long long l_off = STRIDED ? batch * pr.l_sb + hd * pr.l_sh : (long long)bh * Nq;
+      if (g == 0) pr.lse[l_off + query] = (m[qb] + log2f(lt)) * kLn2;
     }
   }
 }

@@ -39,7 +39,9 @@ enum fa_status {
   FA_ERR_ALIAS = 7,      /* out or lse overlaps q, k, v or each other             */
   FA_ERR_NO_DEVICE = 8,  /* no current HIP device, or it is not gfx950            */
   FA_ERR_LAUNCH = 9,     /* the kernel launch was rejected by the HIP runtime     */
-  FA_ERR_INTERNAL = 10   /* anything else (no C++ exception crosses this ABI)     */
+  FA_ERR_INTERNAL = 10,  /* anything else (no C++ exception crosses this ABI)     */
+  FA_ERR_STRIDE = 11     /* a stride is negative, misaligned, smaller than a row, or
+                            puts a head beyond the 32-bit addressing of one head  */
 };
 
 /*
@@ -85,6 +87,46 @@ typedef struct fa_tile_cfg {
 int fa_fwd_cfg(const void *q, const void *k, const void *v, void *out, float *lse,
                int B, int H, int N, int d, float scale, int causal, void *stream,
                const fa_tile_cfg *cfg);
+
+/*
+ * General layouts and lengths: N_q query rows attend over N_k key rows, and
+ * every tensor is addressed by element strides.  Same operation as fa_fwd with
+ * A(i) = {0 .. N_k-1}, or, when causal, {j < N_k : j <= i}: the top-left
+ * alignment of the causal mask, under which every query row sees at least key
+ * 0 (the convention a non-square causal check uses in "How to profile and
+ * optimise kernels", dev.to, Round 4, causal tile-skipping; N_QUERIES and
+ * N_KEYS are separate lengths in "FlashAttention 2 from PyTorch to Triton").
+ *
+ *   q    bf16, element (b, h, i, c) at q[b*q_stride[0] + h*q_stride[1] + i*q_stride[2] + c],
+ *        i < Nq;  k, v likewise with i < Nk;  out like q.  The head dimension is
+ *        contiguous.  A [B, N, H, d] tensor has strides {N*H*d, d, H*d}.
+ *   lse  fp32, element (b, h, i) at lse[b*lse_stride[0] + h*lse_stride[1] + i].
+ *
+ * Stride rules (else FA_ERR_STRIDE): every stride >= 0 and a multiple of 8
+ * elements (16 bytes), every row stride >= d, and (N + 256) * row stride < 2^30
+ * for each tensor's own N, so that one head stays within 32-bit byte offsets.
+ * lse strides >= 0.  Pointers: q, k, v, out 16-byte aligned, lse 4-byte.
+ * Aliasing (FA_ERR_ALIAS) is judged on each tensor's whole byte extent: out
+ * and lse must not overlap q, k, v or each other (inputs may overlap each
+ * other, e.g. three views of one packed QKV tensor).
+ * Other arguments, ownership, asynchrony and determinism as for fa_fwd.
+ */
+typedef struct fa_fwd_desc {
+  const void *q, *k, *v;
+  void *out;
+  float *lse;
+  int B, H, Nq, Nk, d;
+  long long q_stride[3], k_stride[3], v_stride[3], o_stride[3];
+  long long lse_stride[2];
+  float scale;
+  int causal;
+  void *stream;
+} fa_fwd_desc;
+
+int fa_fwd_ex(const fa_fwd_desc *desc);
+
+/* fa_fwd_ex with an explicit tile configuration (FA_ERR_ARG if NULL or not compiled in). */
+int fa_fwd_ex_cfg(const fa_fwd_desc *desc, const fa_tile_cfg *cfg);
 
 /* The configuration fa_fwd picks for (N, d, causal); FA_OK or an error code. */
 int fa_default_cfg(int N, int d, int causal, fa_tile_cfg *cfg);

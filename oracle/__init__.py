@@ -50,6 +50,12 @@ def _load():
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                 ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
                 ctypes.c_void_p, ctypes.c_void_p]
+            lib.oracle_attention_rows_qk.restype = ctypes.c_int
+            lib.oracle_attention_rows_qk.argtypes = [
+                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                ctypes.c_void_p, ctypes.c_void_p]
             lib.oracle_num_threads.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -63,27 +69,30 @@ def num_threads() -> int:
 def attention_rows(q, k, v, scale: float, causal: bool, rows=None):
     """Exact attention for selected query rows, in fp64.
 
-    ``q, k, v``: uint16 bfloat16 bit arrays shaped [B, H, N, d] (contiguous).
-    ``scale``: the softmax scale (a Python float; pass the fp32 value the GPU
-    receives, widened).  ``rows``: flat row ids ``(b*H + h)*N + i``; ``None``
-    means every row.  Returns ``(out [nrows, d] float64, lse [nrows] float64)``.
+    ``q``: uint16 bfloat16 bit array [B, H, Nq, d]; ``k, v``: [B, H, Nk, d]
+    (contiguous).  Causal masking is top-left (key j visible to query i iff
+    j <= i).  ``scale``: the softmax scale (a Python float; pass the fp32 value
+    the GPU receives, widened).  ``rows``: flat query row ids
+    ``(b*H + h)*Nq + i``; ``None`` means every row.  Returns
+    ``(out [nrows, d] float64, lse [nrows] float64)``.
     """
     q = np.ascontiguousarray(q, dtype=np.uint16)
     k = np.ascontiguousarray(k, dtype=np.uint16)
     v = np.ascontiguousarray(v, dtype=np.uint16)
-    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError("q, k, v must share one [B, H, N, d] shape")
-    B, H, N, d = q.shape
+    if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError("q must be [B, H, Nq, d] and k, v one [B, H, Nk, d] shape")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
     if rows is None:
-        rows = np.arange(B * H * N, dtype=np.int64)
+        rows = np.arange(B * H * Nq, dtype=np.int64)
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     out = np.empty((rows.size, d), dtype=np.float64)
     lse = np.empty(rows.size, dtype=np.float64)
-    rc = _load().oracle_attention_rows(
-        q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, N, d, float(scale), int(bool(causal)),
+    rc = _load().oracle_attention_rows_qk(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, Nq, Nk, d, float(scale), int(bool(causal)),
         rows.ctypes.data, rows.size, out.ctypes.data, lse.ctypes.data)
     if rc != 0:
-        raise RuntimeError("oracle_attention_rows failed with code %d" % rc)
+        raise RuntimeError("oracle_attention_rows_qk failed with code %d" % rc)
     return out, lse
 
 

@@ -56,24 +56,29 @@ int oracle_num_threads(void) {
 }
 
 /*
- * rows: flat row ids r = (b * H + h) * N + i, any order, each in [0, B*H*N).
- * out:  nrows * d doubles (row-major), lse: nrows doubles.
+ * Nq query rows over Nk key rows per head (q [B, H, Nq, d], k and v [B, H, Nk, d]).
+ * Permitted keys of query i: all j < Nk, or when causal j <= i as well (the
+ * top-left alignment of the causal mask when Nq != Nk, the convention the
+ * non-square causal check of "How to profile and optimise kernels" (dev.to,
+ * Round 4, causal tile-skipping) compares against; every row keeps key 0).
+ * rows: flat query row ids r = (b * H + h) * Nq + i, any order, each in
+ * [0, B*H*Nq).  out: nrows * d doubles (row-major), lse: nrows doubles.
  * Returns 0 on success, 1 on a bad argument, 2 if scratch memory is exhausted.
  */
-int oracle_attention_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                          int64_t B, int64_t H, int64_t N, int64_t d, double scale,
-                          int causal, const int64_t *rows, int64_t nrows,
-                          double *out, double *lse) {
+int oracle_attention_rows_qk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, double scale,
+                             int causal, const int64_t *rows, int64_t nrows,
+                             double *out, double *lse) {
   if (!q || !k || !v || !rows || !out || !lse) return 1;
-  if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || nrows < 0) return 1;
-  const int64_t total_rows = B * H * N;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || nrows < 0) return 1;
+  const int64_t total_rows = B * H * Nq;
   for (int64_t t = 0; t < nrows; ++t)
     if (rows[t] < 0 || rows[t] >= total_rows) return 1;
 
   int failed = 0;
 #pragma omp parallel
   {
-    double *s = (double *)malloc((size_t)N * sizeof(double));
+    double *s = (double *)malloc((size_t)Nk * sizeof(double));
     double *qi = (double *)malloc((size_t)d * sizeof(double));
     if (!s || !qi) {
 #pragma omp atomic write
@@ -82,11 +87,12 @@ int oracle_attention_rows(const uint16_t *q, const uint16_t *k, const uint16_t *
 #pragma omp for schedule(dynamic, 1)
       for (int64_t t = 0; t < nrows; ++t) {
         const int64_t r = rows[t];
-        const int64_t head = r / N;      /* b * H + h */
-        const int64_t i = r % N;         /* query position */
-        const uint16_t *kh = k + head * N * d;
-        const uint16_t *vh = v + head * N * d;
-        const int64_t nkeys = causal ? i + 1 : N;  /* keys 0 .. nkeys-1 */
+        const int64_t head = r / Nq;     /* b * H + h */
+        const int64_t i = r % Nq;        /* query position */
+        const uint16_t *kh = k + head * Nk * d;
+        const uint16_t *vh = v + head * Nk * d;
+        /* keys 0 .. nkeys-1 */
+        const int64_t nkeys = (causal && i + 1 < Nk) ? i + 1 : Nk;
 
         for (int64_t c = 0; c < d; ++c) qi[c] = oracle_bf16_to_f64(q[r * d + c]);
 
@@ -118,4 +124,12 @@ int oracle_attention_rows(const uint16_t *q, const uint16_t *k, const uint16_t *
     free(qi);
   }
   return failed ? 2 : 0;
+}
+
+/* The square case, N queries over N keys: rows r = (b * H + h) * N + i. */
+int oracle_attention_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                          int64_t B, int64_t H, int64_t N, int64_t d, double scale,
+                          int causal, const int64_t *rows, int64_t nrows,
+                          double *out, double *lse) {
+  return oracle_attention_rows_qk(q, k, v, B, H, N, N, d, scale, causal, rows, nrows, out, lse);
 }

@@ -41,7 +41,7 @@ def test_exported_symbols_have_c_linkage():
 
 def test_strerror_and_version(lib):
     assert fa.version() >= 100
-    for code in range(11):
+    for code in range(12):
         assert fa.strerror(code)
     assert fa.strerror(99) == "unknown status"
 
@@ -102,3 +102,79 @@ def test_no_undefined_kernel_launch_stubs():
     template body the host pass cannot instantiate leaves it undefined)."""
     out = os.popen("nm -D %s" % fa.LIB).read()
     assert not re.findall(r"\bU \S*device_stub\S*", out)
+
+
+# ---------------------------------------------------------------- general-layout entry point
+
+def test_desc_layout_matches_the_header(tmp_path):
+    """The ctypes mirror of fa_fwd_desc has the C struct's size and offsets."""
+    src = tmp_path / "sz.c"
+    src.write_text(
+        "#include <stdio.h>\n#include <stddef.h>\n#include \"fa_fwd.h\"\n"
+        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu\\n\", sizeof(fa_fwd_desc),"
+        " offsetof(fa_fwd_desc, B), offsetof(fa_fwd_desc, q_stride), offsetof(fa_fwd_desc, lse_stride),"
+        " offsetof(fa_fwd_desc, scale), offsetof(fa_fwd_desc, stream)); return 0;}\n")
+    exe = tmp_path / "sz"
+    assert os.system("gcc -I %s -o %s %s" % (os.path.join(ROOT, "include"), exe, src)) == 0
+    got = [int(x) for x in os.popen(str(exe)).read().split()]
+    D = fa.FwdDesc
+    assert got == [ctypes.sizeof(D), D.B.offset, D.q_stride.offset, D.lse_stride.offset, D.scale.offset,
+                   D.stream.offset]
+
+
+def desc(**kw):
+    """A valid square contiguous descriptor on fake pointers, then overrides."""
+    B, H, Nq, Nk, d = kw.pop("B", 1), kw.pop("H", 2), kw.pop("Nq", 64), kw.pop("Nk", 64), kw.pop("d", 64)
+    a = fa.FwdDesc()
+    a.q, a.k, a.v, a.out, a.lse = FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 5 * FAKE
+    a.B, a.H, a.Nq, a.Nk, a.d = B, H, Nq, Nk, d
+    a.q_stride = (ctypes.c_longlong * 3)(H * Nq * d, Nq * d, d)
+    a.o_stride = (ctypes.c_longlong * 3)(H * Nq * d, Nq * d, d)
+    a.k_stride = (ctypes.c_longlong * 3)(H * Nk * d, Nk * d, d)
+    a.v_stride = (ctypes.c_longlong * 3)(H * Nk * d, Nk * d, d)
+    a.lse_stride = (ctypes.c_longlong * 2)(H * Nq, Nq)
+    a.scale, a.causal, a.stream = 0.125, 0, None
+    for key, val in kw.items():
+        if key.endswith("stride"):
+            val = (ctypes.c_longlong * len(val))(*val)
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(lse=None), 1),
+    (dict(Nq=0), 2), (dict(Nk=0), 2), (dict(B=0), 2),
+    (dict(d=96), 3),
+    (dict(q_stride=(8192, 4096, 32)), 11),            # row stride shorter than a row
+    (dict(k_stride=(8192, 4096, 68)), 11),            # not a multiple of 8 elements
+    (dict(v_stride=(8192, -4096, 64)), 11),           # negative
+    (dict(o_stride=(8192, 4096, 1 << 24)), 11),       # a head beyond 32-bit offsets
+    (dict(lse_stride=(-1, 64)), 11),
+    (dict(scale=0.0), 4), (dict(causal=3), 5),
+    (dict(k=2 * FAKE + 8), 6), (dict(lse=5 * FAKE + 2), 6),
+    (dict(out=3 * FAKE), 7), (dict(lse=FAKE + 256), 7),
+])
+def test_desc_argument_errors(lib, kw, code):
+    assert fa.fa_fwd_ex_ptr(desc(**kw)) == code
+
+
+def test_desc_null_and_unknown_cfg(lib):
+    assert lib.fa_fwd_ex(None) == 1
+    assert fa.fa_fwd_ex_ptr(desc(), cfg=(3, 4, 64)) == 5
+
+
+def test_desc_valid_layouts_reach_the_device_check(lib):
+    """Legal descriptors pass validation and stop at the device check here:
+    non-square, [B, N, H, d] strides, and q, k, v as views of one packed tensor."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    B, H, N, d = 2, 4, 128, 64
+    bnhd = (N * H * d, d, H * d)
+    assert fa.fa_fwd_ex_ptr(desc(Nq=17, Nk=300)) == 8
+    assert fa.fa_fwd_ex_ptr(desc(B=B, H=H, Nq=N, Nk=N, q_stride=bnhd, k_stride=bnhd, v_stride=bnhd,
+                                 o_stride=bnhd, out=8 * FAKE)) == 8
+    packed = (N * 3 * H * d, d, 3 * H * d)  # [B, N, 3, H, d]: q, k, v interleaved
+    assert fa.fa_fwd_ex_ptr(desc(B=B, H=H, Nq=N, Nk=N, q=FAKE, k=FAKE + 2 * H * d, v=FAKE + 4 * H * d,
+                                 q_stride=packed, k_stride=packed, v_stride=packed, out=16 * FAKE,
+                                 lse=24 * FAKE)) == 8

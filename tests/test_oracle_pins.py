@@ -264,6 +264,46 @@ def test_brute_force_tiny(B, H, N, d, causal):
             assert abs(lse[t] - L) < 1e-12
 
 
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal", [(1, 1, 5, 17, 8, False), (1, 1, 5, 17, 8, True),
+                                                (2, 1, 19, 6, 16, True), (1, 2, 19, 6, 16, False),
+                                                (1, 1, 1, 40, 64, True), (1, 1, 40, 1, 64, True)])
+def test_brute_force_nonsquare(B, H, Nq, Nk, d, causal):
+    """Nq queries over Nk keys; causal is top-left: query i sees keys 0..min(i, Nk-1)
+    ("How to profile and optimise kernels", Round 4: the non-square causal check
+    against an explicit top-left mask)."""
+    q, _, _ = random_qkv(300 + Nq, B, H, Nq, d)
+    _, k, v = random_qkv(400 + Nk, B, H, Nk, d)
+    scale = f32(1 / math.sqrt(d))
+    out, lse = oracle.attention_rows(q, k, v, scale, causal)
+    qf = bf16_bits_to_f64(q).reshape(B * H, Nq, d)
+    kf, vf = (bf16_bits_to_f64(a).reshape(B * H, Nk, d) for a in (k, v))
+    for bh in range(B * H):
+        for i in range(Nq):
+            n = min(i + 1, Nk) if causal else Nk
+            o, L = brute_force_row(qf[bh, i], kf[bh], vf[bh], scale, n)
+            t = bh * Nq + i
+            assert np.allclose(out[t], o, atol=1e-13, rtol=1e-12)
+            assert abs(lse[t] - L) < 1e-12
+
+
+def test_nonsquare_identical_keys():
+    """Identical keys, more queries than keys, causal: row i averages the first
+    min(i+1, Nk) value rows exactly and LSE = s + ln(count)."""
+    rng = np.random.default_rng(5)
+    Nq, Nk, d = 12, 5, 16
+    scale = f32(0.25)
+    qb = f64_to_bf16_bits(rng.standard_normal((Nq, d))).reshape(1, 1, Nq, d)
+    kv = f64_to_bf16_bits(rng.standard_normal(d))
+    kb = np.tile(kv, (Nk, 1)).reshape(1, 1, Nk, d)
+    vb = f64_to_bf16_bits(rng.standard_normal((Nk, d))).reshape(1, 1, Nk, d)
+    out, lse = oracle.attention_rows(qb, kb, vb, scale, True)
+    qf, kf, vf = bf16_bits_to_f64(qb)[0, 0], bf16_bits_to_f64(kv), bf16_bits_to_f64(vb)[0, 0]
+    for i in range(Nq):
+        n = min(i + 1, Nk)
+        assert np.allclose(out[i], vf[:n].mean(axis=0), atol=1e-13)
+        assert abs(lse[i] - (scale * float(qf[i] @ kf) + math.log(n))) < 1e-12
+
+
 def test_library_softmax_on_asymmetric_case():
     """scipy's softmax/logsumexp on Q K^T (not K Q^T): catches a transposed
     operand, since Q != K here."""
