@@ -13,15 +13,17 @@ import threading
 
 from .buildlib import LIB, build  # noqa: F401
 
-__all__ = ["fa_fwd", "fa_fwd_ptr", "fa_fwd_cfg", "fa_fwd_ex", "fa_fwd_ex_ptr", "FwdDesc", "FaError", "strerror",
+__all__ = ["fa_fwd", "fa_fwd_ptr", "fa_fwd_cfg", "fa_fwd_ex", "fa_fwd_ex_ptr", "fa_fwd_splitkv",
+           "splitkv_workspace_bytes", "splitkv_default_splits", "FwdDesc", "FaError", "strerror",
            "version", "default_cfg", "variants", "load_library", "EXPORTED_SYMBOLS"]
 
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_cfg", "fa_fwd_ex", "fa_fwd_ex_cfg", "fa_default_cfg", "fa_num_variants",
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_cfg", "fa_fwd_ex", "fa_fwd_ex_cfg", "fa_fwd_splitkv",
+                    "fa_splitkv_workspace_bytes", "fa_splitkv_default_splits", "fa_default_cfg", "fa_num_variants",
                     "fa_variant", "fa_strerror", "fa_version")
 
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD_DIM", 4: "FA_ERR_SCALE",
           5: "FA_ERR_ARG", 6: "FA_ERR_ALIGN", 7: "FA_ERR_ALIAS", 8: "FA_ERR_NO_DEVICE",
-          9: "FA_ERR_LAUNCH", 10: "FA_ERR_INTERNAL", 11: "FA_ERR_STRIDE"}
+          9: "FA_ERR_LAUNCH", 10: "FA_ERR_INTERNAL", 11: "FA_ERR_STRIDE", 12: "FA_ERR_WORKSPACE"}
 
 
 class FaError(RuntimeError):
@@ -76,6 +78,12 @@ def load_library():
             lib.fa_fwd_ex.restype = _I
             lib.fa_fwd_ex_cfg.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(TileCfg)]
             lib.fa_fwd_ex_cfg.restype = _I
+            lib.fa_fwd_splitkv.argtypes = [ctypes.POINTER(FwdDesc), _I, _P, ctypes.c_longlong]
+            lib.fa_fwd_splitkv.restype = _I
+            lib.fa_splitkv_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
+            lib.fa_splitkv_workspace_bytes.restype = ctypes.c_longlong
+            lib.fa_splitkv_default_splits.argtypes = [_I, _I, _I, _I, _I, _I]
+            lib.fa_splitkv_default_splits.restype = _I
             lib.fa_default_cfg.argtypes = [_I, _I, _I, ctypes.POINTER(TileCfg)]
             lib.fa_default_cfg.restype = _I
             lib.fa_num_variants.argtypes = []
@@ -185,17 +193,8 @@ def fa_fwd_ex_ptr(desc: FwdDesc, cfg=None) -> int:
     return int(lib.fa_fwd_ex_cfg(ctypes.byref(desc), ctypes.byref(c)))
 
 
-def fa_fwd_ex(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse=None,
-              stream=None, cfg=None):
-    """Attention forward on strided torch bf16 views, N_q queries over N_k keys.
-
-    ``q`` is [B, H, Nq, d] and ``k``, ``v`` are [B, H, Nk, d], each with any
-    strides whose last one is 1 (a [B, N, H, d] tensor is passed as
-    ``t.transpose(1, 2)``).  Causal masking is top-left: key j is visible to
-    query i iff j <= i.  ``out`` (default: a new contiguous tensor) is a
-    [B, H, Nq, d] bf16 view, ``lse`` a [B, H, Nq] fp32 view with unit row stride.
-    Returns ``(out, lse)``; enqueued on ``stream`` (default: the current stream).
-    """
+def _make_desc(q, k, v, scale, causal, out, lse, stream):
+    """Check torch views and fill an ``FwdDesc``; returns ``(desc, out, lse)``."""
     import torch
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape != v.shape:
         raise ValueError("q must be [B, H, Nq, d], k and v one [B, H, Nk, d] shape")
@@ -228,5 +227,52 @@ def fa_fwd_ex(q, k, v, scale: float | None = None, causal: bool = False, out=Non
     desc.scale = float(scale)
     desc.causal = int(bool(causal))
     desc.stream = _stream_handle(stream, q.device)
+    return desc, out, lse
+
+
+def fa_fwd_ex(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse=None,
+              stream=None, cfg=None):
+    """Attention forward on strided torch bf16 views, N_q queries over N_k keys.
+
+    ``q`` is [B, H, Nq, d] and ``k``, ``v`` are [B, H, Nk, d], each with any
+    strides whose last one is 1 (a [B, N, H, d] tensor is passed as
+    ``t.transpose(1, 2)``).  Causal masking is top-left: key j is visible to
+    query i iff j <= i.  ``out`` (default: a new contiguous tensor) is a
+    [B, H, Nq, d] bf16 view, ``lse`` a [B, H, Nq] fp32 view with unit row stride.
+    Returns ``(out, lse)``; enqueued on ``stream`` (default: the current stream).
+    """
+    desc, out, lse = _make_desc(q, k, v, scale, causal, out, lse, stream)
     _check(fa_fwd_ex_ptr(desc, None if cfg is None else tuple(cfg)))
+    return out, lse
+
+
+def splitkv_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int, num_splits: int = 0) -> int:
+    n = int(load_library().fa_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits))
+    if n < 0:
+        _check(-n)
+    return n
+
+
+def splitkv_default_splits(B: int, H: int, Nq: int, Nk: int, d: int, causal: bool = False) -> int:
+    n = int(load_library().fa_splitkv_default_splits(B, H, Nq, Nk, d, int(bool(causal))))
+    if n < 0:
+        _check(-n)
+    return n
+
+
+def fa_fwd_splitkv(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse=None,
+                   stream=None, num_splits: int = 0, workspace=None):
+    """``fa_fwd_ex`` computed over key splits and merged (Flash-Decoding).
+
+    ``workspace``: a device tensor of at least ``splitkv_workspace_bytes(...)``
+    bytes (default: allocated here through torch).  Returns ``(out, lse)``.
+    """
+    import torch
+    desc, out, lse = _make_desc(q, k, v, scale, causal, out, lse, stream)
+    need = splitkv_workspace_bytes(desc.B, desc.H, desc.Nq, desc.Nk, desc.d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(int(load_library().fa_fwd_splitkv(ctypes.byref(desc), int(num_splits), _P(workspace.data_ptr()),
+                                             ctypes.c_longlong(nbytes))))
     return out, lse

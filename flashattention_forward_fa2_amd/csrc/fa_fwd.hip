@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -22,22 +23,33 @@ struct Variant {
   int d, causal, qb, waves, bk;
   Launcher launch;          // contiguous [B, H, N, d] tensors
   Launcher launch_strided;  // any strides
+  Launcher launch_split;    // any strides, one key split per workgroup (p.nsplit splits)
 };
 
-template <int D, bool CAUSAL, int QB, int WAVES, int BK, bool STRIDED>
+template <int D, bool CAUSAL, int QB, int WAVES, int BK, bool STRIDED, bool SPLIT>
 hipError_t launch_variant(const fa::Params& p, int B, hipStream_t stream) {
   using T = fa::Tile<D, QB, WAVES, BK>;
   fa::Params pr = p;
   pr.nqt = (p.Nq + T::kBQ - 1) / T::kBQ;
-  const long long blocks = (long long)B * p.H * pr.nqt;
+  const long long blocks = (long long)B * p.H * pr.nqt * (SPLIT ? p.nsplit : 1);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fa::fa_fwd_kernel<D, CAUSAL, QB, WAVES, BK, STRIDED>), dim3((unsigned)blocks), dim3(T::kThreads), 0,
-                     stream, pr);
+  hipLaunchKernelGGL((fa::fa_fwd_kernel<D, CAUSAL, QB, WAVES, BK, STRIDED, SPLIT>), dim3((unsigned)blocks),
+                     dim3(T::kThreads), 0, stream, pr);
   return hipGetLastError();
 }
 
-#define FA_VARIANT(D, C, QB, W, BK) \
-  {D, C, QB, W, BK, &launch_variant<D, (C) != 0, QB, W, BK, false>, &launch_variant<D, (C) != 0, QB, W, BK, true>}
+template <int D>
+hipError_t launch_merge(const fa::Params& p, hipStream_t stream) {
+  const long long rows = (long long)p.BH * p.Nq;
+  const long long blocks = (rows + (256 / (D / 4)) - 1) / (256 / (D / 4));
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fa::fa_merge_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream, p, rows);
+  return hipGetLastError();
+}
+
+#define FA_VARIANT(D, C, QB, W, BK)                                                                      \
+  {D, C, QB, W, BK, &launch_variant<D, (C) != 0, QB, W, BK, false, false>,                               \
+   &launch_variant<D, (C) != 0, QB, W, BK, true, false>, &launch_variant<D, (C) != 0, QB, W, BK, true, true>}
 #define FA_VARIANTS_DC(D, C) \
   FA_VARIANT(D, C, 1, 4, 64), FA_VARIANT(D, C, 2, 4, 64), FA_VARIANT(D, C, 1, 8, 64)
 
@@ -134,13 +146,8 @@ int validate_desc(const fa_fwd_desc& a) {
   return FA_OK;
 }
 
-int run_desc(const fa_fwd_desc& a, const fa_tile_cfg& cfg) {
-  const int st = validate_desc(a);
-  if (st != FA_OK) return st;
-  const Variant* var = find_variant(a.d, a.causal, cfg);
-  if (!var) return FA_ERR_ARG;
-  const int dst = check_device();
-  if (dst != FA_OK) return dst;
+// Kernel arguments of a (validated) descriptor.
+fa::Params make_params(const fa_fwd_desc& a) {
   fa::Params p{};
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
@@ -156,6 +163,18 @@ int run_desc(const fa_fwd_desc& a, const fa_tile_cfg& cfg) {
   // Scores are kept raw; exp(scale*s - m) = 2^(s*scale*log2(e) - m') with m' in
   // log2 units, so the scale and log2(e) fold into one constant.
   p.qk_scale = (float)((double)a.scale * 1.4426950408889634);
+  p.nsplit = 1;
+  return p;
+}
+
+int run_desc(const fa_fwd_desc& a, const fa_tile_cfg& cfg) {
+  const int st = validate_desc(a);
+  if (st != FA_OK) return st;
+  const Variant* var = find_variant(a.d, a.causal, cfg);
+  if (!var) return FA_ERR_ARG;
+  const int dst = check_device();
+  if (dst != FA_OK) return dst;
+  fa::Params p = make_params(a);
   auto contiguous = [&](const long long st[3], int n) {
     return st[0] == (long long)a.H * n * a.d && st[1] == (long long)n * a.d && st[2] == a.d;
   };
@@ -163,6 +182,62 @@ int run_desc(const fa_fwd_desc& a, const fa_tile_cfg& cfg) {
                      contiguous(a.o_stride, a.Nq) && a.lse_stride[0] == (long long)a.H * a.Nq &&
                      a.lse_stride[1] == a.Nq;
   const hipError_t e = (dense ? var->launch : var->launch_strided)(p, a.B, static_cast<hipStream_t>(a.stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// ---- key splits -------------------------------------------------------------------
+// Keys per split: Nk / S rounded up to whole key tiles of 64.
+constexpr int kSplitTile = 64;
+int split_chunk(int Nk, int S) {
+  const int c = (Nk + S - 1) / S;
+  return (c + kSplitTile - 1) / kSplitTile * kSplitTile;
+}
+int split_count(int Nk, int S) {
+  const int c = split_chunk(Nk, S);
+  return (Nk + c - 1) / c;
+}
+long long split_workspace(int B, int H, int Nq, int d, int S_eff) {
+  return (long long)S_eff * B * H * Nq * (d + 1) * 4;
+}
+
+// (the same for both masks, so the workspace query needs no causal flag)
+int default_splits(int B, int H, int Nq, int Nk, int d) {
+  const fa_tile_cfg c = default_cfg(Nk, d, 0);
+  const long long wgs = (long long)B * H * ((Nq + c.waves * c.qb * 32 - 1) / (c.waves * c.qb * 32));
+  long long s = (512 + wgs - 1) / wgs;       // about two workgroups per CU
+  s = std::min<long long>(s, std::max(1, Nk / 256));  // at least 256 keys per split
+  return (int)std::max<long long>(1, std::min<long long>(s, 1024));
+}
+
+int run_splitkv(const fa_fwd_desc& a, int num_splits, void* ws, long long ws_bytes) {
+  const int st = validate_desc(a);
+  if (st != FA_OK) return st;
+  if (num_splits < 0 || num_splits > 1024) return FA_ERR_ARG;
+  const int S = num_splits ? num_splits : default_splits(a.B, a.H, a.Nq, a.Nk, a.d);
+  const int S_eff = split_count(a.Nk, S);
+  const long long need = split_workspace(a.B, a.H, a.Nq, a.d, S_eff);
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) != 0 || ws_bytes < need) return FA_ERR_WORKSPACE;
+  const std::pair<const void*, long long> others[5] = {
+      {a.q, extent_bytes(a.q_stride, a.B, a.H, a.Nq, a.d, 2)},
+      {a.k, extent_bytes(a.k_stride, a.B, a.H, a.Nk, a.d, 2)},
+      {a.v, extent_bytes(a.v_stride, a.B, a.H, a.Nk, a.d, 2)},
+      {a.out, extent_bytes(a.o_stride, a.B, a.H, a.Nq, a.d, 2)},
+      {a.lse, 4 * ((long long)(a.B - 1) * a.lse_stride[0] + (long long)(a.H - 1) * a.lse_stride[1] + a.Nq)}};
+  for (const auto& o : others)
+    if (overlaps(ws, (size_t)need, o.first, (size_t)o.second)) return FA_ERR_ALIAS;
+  const fa_tile_cfg cfg = default_cfg(a.Nk, a.d, a.causal);
+  const Variant* var = find_variant(a.d, a.causal, cfg);
+  if (!var) return FA_ERR_INTERNAL;
+  const int dst = check_device();
+  if (dst != FA_OK) return dst;
+  fa::Params p = make_params(a);
+  p.nsplit = S_eff;
+  p.chunk = split_chunk(a.Nk, S);
+  p.part_o = static_cast<float*>(ws);
+  p.part_lse = p.part_o + (long long)S_eff * a.B * a.H * a.Nq * a.d;
+  const hipStream_t stream = static_cast<hipStream_t>(a.stream);
+  hipError_t e = var->launch_split(p, a.B, stream);
+  if (e == hipSuccess) e = a.d == 64 ? launch_merge<64>(p, stream) : launch_merge<128>(p, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -228,6 +303,30 @@ int fa_fwd_ex_cfg(const fa_fwd_desc* desc, const fa_tile_cfg* cfg) {
   }
 }
 
+int fa_splitkv_default_splits(int B, int H, int Nq, int Nk, int d, int causal) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return -FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return -FA_ERR_HEAD_DIM;
+  (void)causal;
+  return default_splits(B, H, Nq, Nk, d);
+}
+
+long long fa_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return -FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return -FA_ERR_HEAD_DIM;
+  if (num_splits < 0 || num_splits > 1024) return -FA_ERR_ARG;
+  const int S = num_splits ? num_splits : default_splits(B, H, Nq, Nk, d);
+  return split_workspace(B, H, Nq, d, split_count(Nk, S));
+}
+
+int fa_fwd_splitkv(const fa_fwd_desc* desc, int num_splits, void* workspace, long long workspace_bytes) {
+  if (!desc) return FA_ERR_NULL;
+  try {
+    return run_splitkv(*desc, num_splits, workspace, workspace_bytes);
+  } catch (...) {
+    return FA_ERR_INTERNAL;
+  }
+}
+
 int fa_default_cfg(int N, int d, int causal, fa_tile_cfg* cfg) {
   if (!cfg) return FA_ERR_NULL;
   if (N < 1) return FA_ERR_SHAPE;
@@ -261,6 +360,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_NO_DEVICE: return "no current HIP device, or it is not gfx950";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_INTERNAL: return "internal error";
+    case FA_ERR_WORKSPACE: return "workspace missing, not 256-byte aligned or smaller than fa_splitkv_workspace_bytes";
     case FA_ERR_STRIDE: return "a stride is negative, not a multiple of 8 elements, shorter than a row, or too large";
     default: return "unknown status";
   }

@@ -51,6 +51,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -138,11 +139,22 @@ struct Params {
   int q_rs, k_rs, v_rs, o_rs;
   int H, BH, Nq, Nk, nqt;
   float qk_scale;
+  // Split keys (SPLIT kernels only): workgroup split s covers keys
+  // [s * chunk, min(Nk, (s + 1) * chunk)) and writes fp32 partial results
+  // part_o [nsplit, BH, Nq, d] (normalised over its keys) and part_lse
+  // [nsplit, BH, Nq] (natural log; -inf for a row that sees none of them).
+  float* part_o;
+  float* part_lse;
+  int chunk, nsplit;
 };
 
 // STRIDED = false: every tensor is contiguous [B, H, N, d] (lse [B, H, Nq]) and
 // the strides in `pr` are ignored; the addressing then needs fewer registers.
-template <int D, bool CAUSAL, int QB, int WAVES, int BK, bool STRIDED>
+// SPLIT = true: one key split per workgroup, partial results to the workspace
+// (the per-worker (m, l, o) states that Flash-Decoding merges afterwards:
+// "FlashAttention and kernels", gtadkapally.com, section "FlashAttention-2, -3,
+// and what came after").
+template <int D, bool CAUSAL, int QB, int WAVES, int BK, bool STRIDED, bool SPLIT = false>
 __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
   using T = Tile<D, QB, WAVES, BK>;
   const int BH = pr.BH, Nq = pr.Nq, Nk = pr.Nk, nqt = pr.nqt;
@@ -166,8 +178,9 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
   // allows, ids are remapped so that each XCD works through a contiguous set of
   // heads (their K/V stay in that XCD's L2).  Causal tiles run longest first,
   // all heads' longest tiles before any shorter one.
-  const int total = gridDim.x;
-  const int i = blockIdx.x;
+  const int split = SPLIT ? (int)(blockIdx.x % pr.nsplit) : 0;
+  const int total = SPLIT ? (int)(gridDim.x / pr.nsplit) : (int)gridDim.x;
+  const int i = SPLIT ? (int)(blockIdx.x / pr.nsplit) : (int)blockIdx.x;
   const bool xcd = (BH % 8) == 0;
   const int t = xcd ? (i & 7) * (total >> 3) + (i >> 3) : i;
   int bh, qt;
@@ -254,13 +267,16 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
     for (int db = 0; db < D / 32; ++db) oacc[qb][db] = f32x16{};
   }
 
-  // Causal (top-left: key j is visible to query i iff j <= i): keys at or
-  // after min(q0 + BQ, Nk) are invisible to the whole tile.
-  const int kend = CAUSAL ? min(q0 + T::kBQ, Nk) : Nk;
-  const int ntiles = (kend + BK - 1) / BK;
+  // This workgroup's keys: [kbeg, klim) (all of them unless split).  Causal
+  // (top-left: key j is visible to query i iff j <= i): keys at or after
+  // q0 + BQ are invisible to the whole tile.
+  const int kbeg = SPLIT ? split * pr.chunk : 0;
+  const int klim = SPLIT ? min(Nk, kbeg + pr.chunk) : Nk;
+  const int kend = CAUSAL ? min(q0 + T::kBQ, klim) : klim;
+  const int ntiles = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
 
   auto issue_tile = [&](int j, int stage) {
-    const uint32_t gk = (uint32_t)(j * BK) * k_rs * 2, gv = (uint32_t)(j * BK) * v_rs * 2;
+    const uint32_t gk = (uint32_t)(kbeg + j * BK) * k_rs * 2, gv = (uint32_t)(kbeg + j * BK) * v_rs * 2;
 #pragma unroll
     for (int n = 0; n < T::kBlocksPerWave; ++n) {
       const int b = wave + WAVES * n;
@@ -315,7 +331,7 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if ((CAUSAL && key > query) || key >= Nk) s[qb][kb][r] = -__builtin_inff();
+            if ((CAUSAL && key > query) || key >= klim) s[qb][kb][r] = -__builtin_inff();
           }
       }
       float mx = fmaxf(s[qb][0][0], s[qb][0][1]);
@@ -366,10 +382,10 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
 
   auto step = [&](int j, int stage) {
     if (j + 1 < ntiles) issue_tile(j + 1, stage ^ 1);
-    const int k0 = j * BK;
+    const int k0 = kbeg + j * BK;
     // Wave-uniform classification of this key tile for this wavefront.
     const bool skip = CAUSAL && (k0 > qw + QB * 32 - 1);
-    const bool masked = (CAUSAL && (k0 + BK - 1 > qw)) || (k0 + BK > Nk);
+    const bool masked = (CAUSAL && (k0 + BK - 1 > qw)) || (k0 + BK > klim);
     if (!skip) compute_tile(stage ? lds1 : lds0, k0, masked);
     // This wave's direct loads into the other stage have landed; after the
     // barrier every wave's have, and every wave is done reading this stage.
@@ -377,15 +393,43 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
     __syncthreads();
   };
 
-  issue_tile(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
+  if (ntiles > 0) {  // uniform over the workgroup
+    issue_tile(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
   int j = 0;
   for (; j + 1 < ntiles; j += 2) {
     step(j, 0);
     step(j + 1, 1);
   }
   if (j < ntiles) step(j, 0);
+
+  if constexpr (SPLIT) {
+    // ---- epilogue of a key split: fp32 O / l and LSE, or 0 and -inf for a row
+    // that saw none of this split's keys ------------------------------------------
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float lt = lane_swap_sum(l[qb]);
+      const bool none = !(lt > 0.f);
+      const float inv = none ? 0.f : 1.0f / lt;
+      const int query = qw + qb * 32 + lr;
+      if (query < Nq) {
+        const long long row = ((long long)split * BH + bh) * Nq + query;
+        float* orow = pr.part_o + row * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            f32x4 w = {oacc[qb][db][4 * rr + 0] * inv, oacc[qb][db][4 * rr + 1] * inv,
+                       oacc[qb][db][4 * rr + 2] * inv, oacc[qb][db][4 * rr + 3] * inv};
+            *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * rr + 4 * g) = w;
+          }
+        if (g == 0) pr.part_lse[row] = none ? -__builtin_inff() : (m[qb] + log2f(lt)) * kLn2;
+      }
+    }
+    return;
+  }
 
   // ---- epilogue: O / l -> bf16, LSE = (m + log2 l) ln 2 ------------------------
 #pragma unroll
@@ -409,6 +453,42 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
       if (g == 0) pr.lse[l_off + query] = (m[qb] + log2f(lt)) * kLn2;
     }
   }
+}
+
+// Combine the key splits of every query row: with M = max_s LSE_s and
+// w_s = exp(LSE_s - M), O = sum_s w_s O_s / sum_s w_s and LSE = M + ln sum_s w_s
+// -- the merge rule of two partial (m, l, o) states ("FlashAttention and
+// kernels", the online max/sum exercise that merges partial states, and the
+// Flash-Decoding paragraph of "FlashAttention-2, -3, and what came after"),
+// applied to states already divided by their own l.  One thread per four
+// consecutive head-dim elements of one row; reads are coalesced along d.
+template <int D>
+__global__ __launch_bounds__(256) void fa_merge_kernel(const Params pr, long long rows) {
+  constexpr int kTPR = D / 4;  // threads per row
+  const long long r = (long long)blockIdx.x * (256 / kTPR) + threadIdx.x / kTPR;
+  const int c = (threadIdx.x % kTPR) * 4;
+  if (r >= rows) return;
+  const int bh = (int)(r / pr.Nq), query = (int)(r - (long long)bh * pr.Nq);
+  const long long plane = (long long)pr.BH * pr.Nq;
+  float mx = -__builtin_inff();
+  for (int s = 0; s < pr.nsplit; ++s) mx = fmaxf(mx, pr.part_lse[s * plane + r]);
+  float wsum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < pr.nsplit; ++s) {
+    const float ls = pr.part_lse[s * plane + r];
+    if (ls == -__builtin_inff()) continue;
+    const float w = expf(ls - mx);
+    wsum += w;
+    acc += w * *reinterpret_cast<const f32x4*>(pr.part_o + (s * plane + r) * D + c);
+  }
+  const float inv = 1.0f / wsum;
+  const int batch = bh / pr.H, hd = bh - batch * pr.H;
+  uint16_t* orow = pr.out + batch * pr.o_sb + hd * pr.o_sh + (long long)query * pr.o_rs;
+  u32x2 w2;
+  w2[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  w2[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<u32x2*>(orow + c) = w2;
+  if (c == 0) pr.lse[batch * pr.l_sb + hd * pr.l_sh + query] = mx + logf(wsum);
 }
 
 }  // namespace fa

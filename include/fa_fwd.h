@@ -40,8 +40,9 @@ enum fa_status {
   FA_ERR_NO_DEVICE = 8,  /* no current HIP device, or it is not gfx950            */
   FA_ERR_LAUNCH = 9,     /* the kernel launch was rejected by the HIP runtime     */
   FA_ERR_INTERNAL = 10,  /* anything else (no C++ exception crosses this ABI)     */
-  FA_ERR_STRIDE = 11     /* a stride is negative, misaligned, smaller than a row, or
+  FA_ERR_STRIDE = 11,    /* a stride is negative, misaligned, smaller than a row, or
                             puts a head beyond the 32-bit addressing of one head  */
+  FA_ERR_WORKSPACE = 12  /* split-key workspace missing, misaligned or too small   */
 };
 
 /*
@@ -127,6 +128,37 @@ int fa_fwd_ex(const fa_fwd_desc *desc);
 
 /* fa_fwd_ex with an explicit tile configuration (FA_ERR_ARG if NULL or not compiled in). */
 int fa_fwd_ex_cfg(const fa_fwd_desc *desc, const fa_tile_cfg *cfg);
+
+/*
+ * Split keys (Flash-Decoding): the same operation as fa_fwd_ex, computed by
+ * splitting each head's keys into S contiguous ranges of whole 64-key tiles;
+ * one pass produces every range's normalised partial output and log-sum-exp,
+ * and a second kernel merges them per query row with the rule that combines
+ * two partial (m, l, o) states ("FlashAttention and kernels", gtadkapally.com:
+ * the online max/sum exercise with its merge of partial states, and the
+ * Flash-Decoding paragraph of "FlashAttention-2, -3, and what came after").
+ * It fills the GPU when B*H*ceil(Nq/256) is small (short prompts, decoding with
+ * few query rows); results agree with fa_fwd_ex to rounding.
+ *
+ *   num_splits  requested S (1..1024), or 0 for fa_splitkv_default_splits; the
+ *               number used is ceil(Nk / chunk) with chunk = ceil(Nk / S)
+ *               rounded up to a multiple of 64 keys.
+ *   workspace   caller-owned device memory, 256-byte aligned, at least
+ *               fa_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits) bytes;
+ *               scratch: its contents on entry are ignored and on return are
+ *               unspecified.  It must not overlap any tensor (FA_ERR_ALIAS), and
+ *               two calls in flight must not share it.
+ * Errors: as fa_fwd_ex, plus FA_ERR_WORKSPACE, and FA_ERR_ARG for num_splits
+ * outside 0..1024.  Two kernels are enqueued on desc->stream.
+ */
+int fa_fwd_splitkv(const fa_fwd_desc *desc, int num_splits, void *workspace, long long workspace_bytes);
+
+/* Workspace bytes for fa_fwd_splitkv (>= 0), or minus an error code. */
+long long fa_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);
+
+/* The split count fa_fwd_splitkv uses for num_splits = 0 (>= 1; about two
+ * workgroups per compute unit, at least 256 keys per split), or minus an error code. */
+int fa_splitkv_default_splits(int B, int H, int Nq, int Nk, int d, int causal);
 
 /* The configuration fa_fwd picks for (N, d, causal); FA_OK or an error code. */
 int fa_default_cfg(int N, int d, int causal, fa_tile_cfg *cfg);

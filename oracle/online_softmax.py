@@ -62,6 +62,26 @@ def update(state: RowState, scores, values) -> RowState:
     return state
 
 
+def merge(a: RowState, b: RowState) -> RowState:
+    """Combine the states of two disjoint key sets of one row: m = max(m_a, m_b),
+    l = l_a e^(m_a - m) + l_b e^(m_b - m), o = o_a e^(m_a - m) + o_b e^(m_b - m).
+    The merge of two partial (m, l) states asked for in "FlashAttention and
+    kernels" (the online max/sum exercise), and the step Flash-Decoding applies
+    to the states of its key splits (same page, "FlashAttention-2, -3, and what
+    came after"); an empty state (m = -inf, l = 0) is its identity."""
+    m = max(a.m, b.m)
+    out = RowState(m=m)
+    if m == -math.inf:
+        out.l, out.o = 0.0, (a.o if a.o is not None else b.o)
+        return out
+    ea, eb = _exp(a.m - m), _exp(b.m - m)
+    out.l = a.l * ea + b.l * eb
+    oa = a.o if a.o is not None else 0.0
+    ob = b.o if b.o is not None else 0.0
+    out.o = oa * ea + ob * eb
+    return out
+
+
 def online_max_sum(xs) -> tuple[float, float]:
     """One element at a time: ``m_new = max(m, x)``, ``l = l e^(m - m_new) + e^(x - m_new)``."""
     m, l = -math.inf, 0.0

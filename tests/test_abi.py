@@ -21,7 +21,7 @@ def lib():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:int|const char \*)\s*\*?\s*(fa_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^(?:int|long long|const char \*)\s*\*?\s*(fa_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_what_the_binding_lists():
@@ -41,7 +41,7 @@ def test_exported_symbols_have_c_linkage():
 
 def test_strerror_and_version(lib):
     assert fa.version() >= 100
-    for code in range(12):
+    for code in range(13):
         assert fa.strerror(code)
     assert fa.strerror(99) == "unknown status"
 
@@ -178,3 +178,43 @@ def test_desc_valid_layouts_reach_the_device_check(lib):
     assert fa.fa_fwd_ex_ptr(desc(B=B, H=H, Nq=N, Nk=N, q=FAKE, k=FAKE + 2 * H * d, v=FAKE + 4 * H * d,
                                  q_stride=packed, k_stride=packed, v_stride=packed, out=16 * FAKE,
                                  lse=24 * FAKE)) == 8
+
+
+# ---------------------------------------------------------------- split keys
+
+def test_splitkv_workspace_and_default_splits(lib):
+    assert fa.splitkv_workspace_bytes(1, 8, 1024, 1024, 64, 4) == 4 * 8 * 1024 * 65 * 4
+    # chunk = ceil(1000 / 3) = 334 -> 384 keys, so 3 splits are used
+    assert fa.splitkv_workspace_bytes(1, 1, 10, 1000, 128, 3) == 3 * 10 * 129 * 4
+    # 16 requested over 100 keys: chunk 64, 2 splits used
+    assert fa.splitkv_workspace_bytes(1, 1, 1, 100, 64, 16) == 2 * 65 * 4
+    assert fa.splitkv_default_splits(1, 8, 1024, 1024, 64) == 4      # 32 workgroups, >= 256 keys per split
+    assert fa.splitkv_default_splits(1, 32, 1, 32768, 128) == 16     # decode: 32 workgroups -> 16 splits
+    assert fa.splitkv_default_splits(4, 8, 4096, 4096, 64) == 1      # 512 workgroups already
+    with pytest.raises(fa.FaError):
+        fa.splitkv_workspace_bytes(1, 1, 1, 1, 96, 1)
+
+
+WS = 64 * FAKE  # 256-byte aligned, far from the tensors
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(ws=None), 12), (dict(ws=WS + 16), 12), (dict(nbytes=100), 12),
+    (dict(splits=-1), 5), (dict(splits=2000), 5),
+    (dict(ws=FAKE), 7),                       # the workspace overlaps q
+])
+def test_splitkv_argument_errors(lib, args, code):
+    d = desc()
+    ws = args.get("ws", WS)
+    nbytes = args.get("nbytes", 1 << 30)
+    st = lib.fa_fwd_splitkv(ctypes.byref(d), args.get("splits", 2), None if ws is None else ctypes.c_void_p(ws),
+                            ctypes.c_longlong(nbytes))
+    assert st == code
+
+
+def test_splitkv_valid_call_reaches_the_device_check(lib):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    d = desc(Nq=1, Nk=4096)
+    assert lib.fa_fwd_splitkv(ctypes.byref(d), 0, ctypes.c_void_p(WS), ctypes.c_longlong(1 << 30)) == 8

@@ -392,3 +392,49 @@ def test_whole_head_recurrence_matches_oracle():
         o_ref, l_ref = oracle.attention_rows(q, k, v, 0.25, causal)
         o, l = osm.attention_recurrence(qf, kf, vf, 0.25, causal, block=16)
         assert np.allclose(o, o_ref, atol=1e-12) and np.allclose(l, l_ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------- merge of partial states
+
+def test_merge_reproduces_the_two_block_example():
+    """The state of block 1 merged with the state block 2 has on its own is the
+    printed state after block 2 (m = ln 2, l = 3, o = [1.5, 1.5]) and O = [1/2, 1/2]
+    ("4 Triton and Custom Kernels", section 4.8 worked example)."""
+    g = load("online_softmax_two_blocks.json")
+    s = [num(x) for x in g["scores"]]
+    V = np.array(g["V"], dtype=float)
+    a = osm.update(osm.RowState(), s[:2], V[:2])
+    b = osm.update(osm.RowState(), s[2:], V[2:])
+    mg = osm.merge(a, b)
+    after = g["printed"]["after_block_2"]
+    assert mg.m == pytest.approx(num(after["m"]), abs=1e-15)
+    assert mg.l == pytest.approx(after["l"], abs=1e-15)
+    assert np.allclose(mg.o, after["o"], atol=1e-15)
+    assert np.allclose(mg.o / mg.l, g["printed"]["output"], atol=1e-15)
+
+
+def test_merge_of_any_split_equals_the_whole_row():
+    """Key splits of any sizes, each run through the recurrence and then merged in
+    any order, give the definition's O and LSE; the empty state is the identity."""
+    rng = np.random.default_rng(9)
+    for trial in range(20):
+        n = int(rng.integers(2, 200))
+        s = list(rng.standard_normal(n) * 4.0)
+        V = rng.standard_normal((n, 8))
+        w = np.exp(np.array(s) - max(s))
+        ref_o, ref_l = (w @ V) / w.sum(), max(s) + math.log(w.sum())
+        cuts = sorted(set(int(c) for c in rng.integers(1, n, size=int(rng.integers(1, 6)))))
+        parts = [(a, b) for a, b in zip([0] + cuts, cuts + [n]) if b > a]
+        states = [osm.update(osm.RowState(), s[a:b], V[a:b]) for a, b in parts]
+        rng.shuffle(states)
+        acc = osm.RowState()
+        for st in states:
+            acc = osm.merge(acc, st)
+        assert np.allclose(acc.o / acc.l, ref_o, atol=1e-12)
+        assert acc.m + math.log(acc.l) == pytest.approx(ref_l, abs=1e-12)
+
+
+def test_merge_with_empty_state_is_identity():
+    a = osm.update(osm.RowState(), [0.5, -1.0], np.eye(2))
+    for m in (osm.merge(a, osm.RowState()), osm.merge(osm.RowState(), a)):
+        assert m.m == a.m and m.l == a.l and np.array_equal(m.o, a.o)
