@@ -38,9 +38,17 @@ METRIC = "attention fwd TFLOP/s (bf16, causal + non-causal) and % of bf16 MFMA p
 PAGES_STEP_TFLOPS = (4 * 32 * 4096 ** 2 * 64 * 1.5) / 3.031e-3 / 1e12
 
 
-def flops(B, H, N, d, causal):
-    f = 4.0 * B * H * N * N * d
-    return f / 2 if causal else f
+def flops(B, H, N, d, causal, Nk=None):
+    """4*B*H*N^2*d, halved for causal (the pages' convention); with Nq != Nk
+    the exact count of visible (query, key) pairs times 4*d."""
+    if Nk is None or Nk == N:
+        f = 4.0 * B * H * N * N * d
+        return f / 2 if causal else f
+    if not causal:
+        return 4.0 * B * H * N * Nk * d
+    m = min(N, Nk)
+    pairs = m * (m + 1) / 2 + (N - m) * Nk  # row i sees min(i + 1, Nk) keys
+    return 4.0 * B * H * pairs * d
 
 
 def parse():
@@ -58,6 +66,10 @@ def parse():
                     help="run one mode only (counter collection)")
     ap.add_argument("--layout", choices=["bhnd", "bnhd"], default="bhnd",
                     help="bnhd: q, k, v, out stored [B, N, H, d] and passed as strided views (fa_fwd_ex)")
+    ap.add_argument("--nq", type=int, default=None,
+                    help="use only the first NQ query rows (Nq != Nk, through fa_fwd_ex)")
+    ap.add_argument("--splitkv", type=int, default=None, metavar="S",
+                    help="run through fa_fwd_splitkv with S key splits (0: the library's default)")
     ap.add_argument("--flush-reps", type=int, default=10,
                     help="launches per mode timed again with caches flushed before each (0: skip)")
     ap.add_argument("--no-gemm", action="store_true", help="skip the attainable-GEMM reference")
@@ -113,6 +125,14 @@ def main():
     t0 = time.time()
     q_bits, k_bits, v_bits = inputs.make_qkv(args.workload)
     print("[bench] inputs %s generated in %.1fs" % (w["name"], time.time() - t0), file=sys.stderr, flush=True)
+    Nk = N
+    if args.nq is not None:
+        if not 1 <= args.nq <= N:
+            print("--nq must be in 1..%d" % N, file=sys.stderr)
+            sys.exit(2)
+        q_bits = np.ascontiguousarray(q_bits[:, :, :args.nq])
+        N = args.nq
+    general = args.layout == "bnhd" or N != Nk or args.splitkv is not None
     to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
     q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
     if args.layout == "bnhd":
@@ -124,8 +144,15 @@ def main():
     lses = {c: torch.empty((B, H, N), dtype=torch.float32, device=dev) for c in modes}
     stream = torch.cuda.current_stream(dev)
 
+    ws = None
+    if args.splitkv is not None:
+        ws = torch.empty(fa.splitkv_workspace_bytes(B, H, N, Nk, d, args.splitkv), dtype=torch.uint8, device=dev)
+
     def launch(c):
-        if args.layout == "bnhd":
+        if args.splitkv is not None:
+            fa.fa_fwd_splitkv(q, k, v, scale=scale, causal=bool(c), out=outs[c], lse=lses[c], stream=stream,
+                              num_splits=args.splitkv, workspace=ws)
+        elif general:
             fa.fa_fwd_ex(q, k, v, scale=scale, causal=bool(c), out=outs[c], lse=lses[c], stream=stream, cfg=cfg)
         else:
             fa.fa_fwd(q, k, v, scale=scale, causal=bool(c), out=outs[c], lse=lses[c], stream=stream, cfg=cfg)
@@ -154,20 +181,20 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
 
-    step_flops = sum(flops(B, H, N, d, c) for c in modes)
+    step_flops = sum(flops(B, H, N, d, c, Nk) for c in modes)
     ms_per_step = wall * 1e3 / args.steps
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     per_mode = {}
     for c in modes:
         ms = np.array([a.elapsed_time(b) for a, b in ev[c]])
         avg = float(ms.mean())
-        tf = flops(B, H, N, d, c) / (avg * 1e-3) / 1e12
+        tf = flops(B, H, N, d, c, Nk) / (avg * 1e-3) / 1e12
         per_mode["causal" if c else "noncausal"] = dict(
             kernel_ms_avg=round(avg, 5), kernel_ms_median=round(float(np.median(ms)), 5),
             kernel_ms_min=round(float(ms.min()), 5), kernel_ms_max=round(float(ms.max()), 5),
             tflops=round(tf, 2),
             frac_of_peak=round(tf / PEAK_BF16_TFLOPS, 4),
-            hbm_gbs=round((8.0 * B * H * N * d + 4.0 * B * H * N) / (avg * 1e-3) / 1e9, 1),
+            hbm_gbs=round((4.0 * B * H * N * d + 4.0 * B * H * Nk * d + 4.0 * B * H * N) / (avg * 1e-3) / 1e9, 1),
             cfg=list(cfg if cfg else fa.default_cfg(N, d, bool(c))))
     # Outside the timed region: each mode again with the caches flushed before
     # every launch (a 512 MiB write, more than L2 and the 256 MB Infinity Cache).
@@ -189,9 +216,9 @@ def main():
     dom = per_mode["causal" if dom_c else "noncausal"]
     roofline = dict(bound="mfma", achieved=dom["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=dom["frac_of_peak"],
-                    traffic=measured_traffic(B, H, N, d, dom_c) if args.layout == "bhnd" else None,
+                    traffic=measured_traffic(B, H, N, d, dom_c) if not general else None,
                     kernel="fa_fwd_kernel d=%d causal=%d cfg=%s" % (d, dom_c, dom["cfg"]),
-                    flops_per_launch=flops(B, H, N, d, dom_c))
+                    flops_per_launch=flops(B, H, N, d, dom_c, Nk))
     if not args.no_gemm:
         g = attainable_gemm(torch, dev)
         roofline["attainable_gemm_tflops"] = g
@@ -205,10 +232,14 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(value / PAGES_STEP_TFLOPS, 3) if args.workload == 3 and len(modes) == 2 else None,
+        "vs_baseline": (round(value / PAGES_STEP_TFLOPS, 3)
+                        if args.workload == 3 and len(modes) == 2 and N == Nk else None),
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "%s %s%s" % (w["name"], "+".join("causal" if c else "non-causal" for c in modes),
-                                            "" if args.layout == "bhnd" else " [B,N,H,d] strided"),
+        "config": {"workload": "%s %s%s%s%s" % (w["name"], "+".join("causal" if c else "non-causal" for c in modes),
+                                                "" if args.layout == "bhnd" else " [B,N,H,d] strided",
+                                                "" if N == Nk else " Nq=%d" % N,
+                                                "" if args.splitkv is None else " split-keys S=%d" % args.splitkv),
+                   "Nq": N, "Nk": Nk,
                    "B": B, "H": H, "N": N, "d": d, "scale": scale, "sigma_qk": w["sigma_qk"],
                    "flops_per_step": step_flops, "modes": per_mode},
         "roofline": roofline,
@@ -258,10 +289,11 @@ def cpu_baseline(args, w, modes, q_bits, k_bits, v_bits, scale, outs, lses):
     import oracle
     from inputs import bf16_bits_to_f64, sample_rows, workload_seed
 
-    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    B, H, d = w["B"], w["H"], w["d"]
+    N, Nk = q_bits.shape[2], k_bits.shape[2]  # query rows, key rows
     # About 250 GFLOP of fp64 oracle work (~10 s on 16 host cores), at most every row.
     mode_weight = sum(0.5 if c else 1.0 for c in modes)
-    per_head = args.cpu_rows_per_head or int(np.clip(250e9 / (B * H * 4.0 * N * d * mode_weight), 16, N))
+    per_head = args.cpu_rows_per_head or int(np.clip(250e9 / (B * H * 4.0 * Nk * d * mode_weight), 16, N))
     if per_head >= N:  # the budget covers the whole workload: every row
         rows = np.arange(B * H * N, dtype=np.int64)
     else:
@@ -273,7 +305,7 @@ def cpu_baseline(args, w, modes, q_bits, k_bits, v_bits, scale, outs, lses):
         t0 = time.perf_counter()
         o_ref, l_ref = oracle.attention_rows(q_bits, k_bits, v_bits, scale, bool(c), rows)
         total_s += time.perf_counter() - t0
-        nkeys = (i + 1) if c else np.full(rows.shape, N)
+        nkeys = np.minimum(i + 1, Nk) if c else np.full(rows.shape, Nk)
         total_flops += float(np.sum(4.0 * nkeys * d))
         o = bf16_bits_to_f64(outs[c].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)).reshape(-1, d)[rows]
         L = lses[c].cpu().numpy().reshape(-1)[rows]

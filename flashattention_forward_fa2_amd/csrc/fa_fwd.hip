@@ -200,9 +200,15 @@ long long split_workspace(int B, int H, int Nq, int d, int S_eff) {
   return (long long)S_eff * B * H * Nq * (d + 1) * 4;
 }
 
+// Tile configuration of the split path: short query ranges (decoding, short
+// prompts) take the 4-wave, 128-query tile, so fewer MFMA rows are padding.
+fa_tile_cfg split_cfg(int Nq, int Nk, int d, int causal) {
+  return Nq <= 128 ? fa_tile_cfg{1, 4, 64} : default_cfg(Nk, d, causal);
+}
+
 // (the same for both masks, so the workspace query needs no causal flag)
 int default_splits(int B, int H, int Nq, int Nk, int d) {
-  const fa_tile_cfg c = default_cfg(Nk, d, 0);
+  const fa_tile_cfg c = split_cfg(Nq, Nk, d, 0);
   const long long wgs = (long long)B * H * ((Nq + c.waves * c.qb * 32 - 1) / (c.waves * c.qb * 32));
   long long s = (512 + wgs - 1) / wgs;       // about two workgroups per CU
   s = std::min<long long>(s, std::max(1, Nk / 256));  // at least 256 keys per split
@@ -225,8 +231,7 @@ int run_splitkv(const fa_fwd_desc& a, int num_splits, void* ws, long long ws_byt
       {a.lse, 4 * ((long long)(a.B - 1) * a.lse_stride[0] + (long long)(a.H - 1) * a.lse_stride[1] + a.Nq)}};
   for (const auto& o : others)
     if (overlaps(ws, (size_t)need, o.first, (size_t)o.second)) return FA_ERR_ALIAS;
-  const fa_tile_cfg cfg = default_cfg(a.Nk, a.d, a.causal);
-  const Variant* var = find_variant(a.d, a.causal, cfg);
+  const Variant* var = find_variant(a.d, a.causal, split_cfg(a.Nq, a.Nk, a.d, a.causal));
   if (!var) return FA_ERR_INTERNAL;
   const int dst = check_device();
   if (dst != FA_OK) return dst;

@@ -157,7 +157,8 @@ int fa_fwd_splitkv(const fa_fwd_desc *desc, int num_splits, void *workspace, lon
 long long fa_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);
 
 /* The split count fa_fwd_splitkv uses for num_splits = 0 (>= 1; about two
- * workgroups per compute unit, at least 256 keys per split), or minus an error code. */
+ * workgroups per compute unit, at least 256 keys per split), or minus an error code.
+ * (The split path runs 128-query workgroups when Nq <= 128, else fa_fwd's tile.) */
 int fa_splitkv_default_splits(int B, int H, int Nq, int Nk, int d, int causal);
 
 /* The configuration fa_fwd picks for (N, d, causal); FA_OK or an error code. */
