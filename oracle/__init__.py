@@ -56,6 +56,11 @@ def _load():
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                 ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
                 ctypes.c_void_p, ctypes.c_void_p]
+            lib.oracle_attention_bwd.restype = ctypes.c_int
+            lib.oracle_attention_bwd.argtypes = [
+                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
             lib.oracle_num_threads.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -94,6 +99,24 @@ def attention_rows(q, k, v, scale: float, causal: bool, rows=None):
     if rc != 0:
         raise RuntimeError("oracle_attention_rows_qk failed with code %d" % rc)
     return out, lse
+
+
+def attention_bwd(q, k, v, dout, scale: float, causal: bool):
+    """Gradients (dq, dk, dv) of sum(dout * out) in fp64, each [B, H, N, d].
+
+    ``q, k, v, dout``: uint16 bfloat16 bit arrays [B, H, N, d] (square heads).
+    Follows ``oracle_attention_bwd`` in ``oracle.c``.
+    """
+    arrs = [np.ascontiguousarray(a, dtype=np.uint16) for a in (q, k, v, dout)]
+    if arrs[0].ndim != 4 or any(a.shape != arrs[0].shape for a in arrs):
+        raise ValueError("q, k, v, dout must share one [B, H, N, d] shape")
+    B, H, N, d = arrs[0].shape
+    dq, dk, dv = (np.empty((B, H, N, d), dtype=np.float64) for _ in range(3))
+    rc = _load().oracle_attention_bwd(*(a.ctypes.data for a in arrs), B, H, N, d, float(scale),
+                                      int(bool(causal)), dq.ctypes.data, dk.ctypes.data, dv.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_attention_bwd failed with code %d" % rc)
+    return dq, dk, dv
 
 
 def attention_f64(q, k, v, scale: float, causal: bool):

@@ -133,3 +133,91 @@ int oracle_attention_rows(const uint16_t *q, const uint16_t *k, const uint16_t *
                           double *out, double *lse) {
   return oracle_attention_rows_qk(q, k, v, B, H, N, N, d, scale, causal, rows, nrows, out, lse);
 }
+
+/*
+ * Gradients of the attention rule with respect to q, k and v, for an upstream
+ * gradient dout of the output: the derivative of sum(dout . out) written out
+ * through the chain rule (the backward pass FlashAttention recomputes from the
+ * saved log-sum-exp: "FlashAttention and kernels" (gtadkapally.com), section
+ * "FlashAttention-2, -3, and what came after", and "Kernels and FlashAttention"
+ * (prathameshsaraf.com), on keeping L for the backward pass):
+ *
+ *   P_ij  = softmax_j(scale q_i . k_j)  over the permitted keys (causal: j <= i)
+ *   dV_j  = sum_i P_ij dout_i
+ *   dP_ij = dout_i . v_j
+ *   D_i   = sum_j P_ij dP_ij
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dQ_i  = scale sum_j dS_ij k_j,    dK_j = scale sum_i dS_ij q_i
+ *
+ * Square heads, contiguous [B, H, N, d] bfloat16 inputs; dq, dk, dv are
+ * B*H*N*d doubles.  One score row at a time (no N x N buffer): the dQ row is
+ * finished per query, dK and dV accumulate over queries; each head is one
+ * OpenMP task, so accumulation order is fixed.  Returns 0, 1 on a bad argument,
+ * 2 if scratch memory is exhausted.
+ */
+int oracle_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                         int64_t B, int64_t H, int64_t N, int64_t d, double scale, int causal,
+                         double *dq, double *dk, double *dv) {
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return 1;
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 1;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double *p = (double *)malloc((size_t)N * sizeof(double));
+    double *dp = (double *)malloc((size_t)N * sizeof(double));
+    double *qi = (double *)malloc((size_t)d * sizeof(double));
+    double *gi = (double *)malloc((size_t)d * sizeof(double));
+    if (!p || !dp || !qi || !gi) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t head = 0; head < B * H; ++head) {
+        const uint16_t *qh = q + head * N * d, *kh = k + head * N * d;
+        const uint16_t *vh = v + head * N * d, *gh = dout + head * N * d;
+        double *dqh = dq + head * N * d, *dkh = dk + head * N * d, *dvh = dv + head * N * d;
+        for (int64_t x = 0; x < N * d; ++x) dkh[x] = dvh[x] = 0.0;
+        for (int64_t i = 0; i < N; ++i) {
+          const int64_t nkeys = causal ? i + 1 : N;
+          for (int64_t c = 0; c < d; ++c) {
+            qi[c] = oracle_bf16_to_f64(qh[i * d + c]);
+            gi[c] = oracle_bf16_to_f64(gh[i * d + c]);
+          }
+          /* probabilities of row i (the forward's definition) */
+          double m = -INFINITY;
+          for (int64_t j = 0; j < nkeys; ++j) {
+            double acc = 0.0;
+            for (int64_t c = 0; c < d; ++c) acc += qi[c] * oracle_bf16_to_f64(kh[j * d + c]);
+            p[j] = scale * acc;
+            if (p[j] > m) m = p[j];
+          }
+          double l = 0.0;
+          for (int64_t j = 0; j < nkeys; ++j) l += exp(p[j] - m);
+          for (int64_t j = 0; j < nkeys; ++j) p[j] = exp(p[j] - m) / l;
+          /* dP_ij = dout_i . v_j and D_i = sum_j P_ij dP_ij */
+          double D = 0.0;
+          for (int64_t j = 0; j < nkeys; ++j) {
+            double acc = 0.0;
+            for (int64_t c = 0; c < d; ++c) acc += gi[c] * oracle_bf16_to_f64(vh[j * d + c]);
+            dp[j] = acc;
+            D += p[j] * acc;
+          }
+          for (int64_t c = 0; c < d; ++c) dqh[i * d + c] = 0.0;
+          for (int64_t j = 0; j < nkeys; ++j) {
+            const double ds = p[j] * (dp[j] - D);
+            for (int64_t c = 0; c < d; ++c) {
+              dvh[j * d + c] += p[j] * gi[c];
+              dqh[i * d + c] += scale * ds * oracle_bf16_to_f64(kh[j * d + c]);
+              dkh[j * d + c] += scale * ds * qi[c];
+            }
+          }
+        }
+      }
+    }
+    free(p);
+    free(dp);
+    free(qi);
+    free(gi);
+  }
+  return failed ? 2 : 0;
+}
