@@ -14,6 +14,7 @@ inputs already resident in HBM.  Prints ONE JSON line:
              the parity of those rows against the GPU output.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3|4|5]
+       python bench.py --bwd ...   (the backward pass instead; its own JSON line)
 """
 from __future__ import annotations
 
@@ -73,6 +74,8 @@ def parse():
     ap.add_argument("--flush-reps", type=int, default=10,
                     help="launches per mode timed again with caches flushed before each (0: skip)")
     ap.add_argument("--no-gemm", action="store_true", help="skip the attainable-GEMM reference")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward (fa_bwd: dQ, dK, dV from the forward's out and LSE) instead")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="instead of attention, run a plain device copy of MIB MiB (calibrates byte counters)")
     return ap.parse_args()
@@ -102,6 +105,9 @@ def main():
 
     if args.copy_calib:
         copy_calibration(args.copy_calib)
+        return
+    if args.bwd:
+        main_bwd(args)
         return
 
     import torch
@@ -242,6 +248,119 @@ def main():
                    "Nq": N, "Nk": Nk,
                    "B": B, "H": H, "N": N, "d": d, "scale": scale, "sigma_qk": w["sigma_qk"],
                    "flops_per_step": step_flops, "modes": per_mode},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+BWD_METRIC = "attention bwd TFLOP/s (bf16, dQ dK dV; 2.5x the forward's FLOPs) and % of bf16 MFMA peak"
+
+
+def main_bwd(args):
+    """The backward pass (three kernels per call) over the workload's modes:
+    out, LSE and dO are computed / drawn before the timed region; one step is
+    one fa_bwd call per mode.  FLOPs are the 5 matrix products of the chain
+    rule, 10*B*H*N^2*d (halved for causal); the dQ pass's recomputation of S and
+    dP is not counted."""
+    import torch
+    import flashattention_forward_fa2_amd as fa
+    import inputs
+
+    fa.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = inputs.WORKLOADS[args.workload]
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    modes = list(w["modes"]) if args.workload != 3 else [0, 1]
+    if args.only:
+        modes = [c for c in modes if c == (args.only == "causal")]
+    scale = inputs.default_scale(d)
+    q_bits, k_bits, v_bits = inputs.make_qkv(args.workload)
+    g_bits = inputs.normal_bf16(inputs.workload_seed(args.workload, 4), B * H * N * d).reshape(B, H, N, d)
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v, dout = (to_dev(a) for a in (q_bits, k_bits, v_bits, g_bits))
+    stream = torch.cuda.current_stream(dev)
+    fw = {c: fa.fa_fwd(q, k, v, scale=scale, causal=bool(c), stream=stream) for c in modes}
+    grads = {c: tuple(torch.empty_like(q) for _ in range(3)) for c in modes}
+    ws = torch.empty(fa.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+
+    def launch(c):
+        fa.fa_bwd(q, k, v, fw[c][0], fw[c][1], dout, scale=scale, causal=bool(c), dq=grads[c][0], dk=grads[c][1],
+                  dv=grads[c][2], workspace=ws, stream=stream)
+
+    for _ in range(max(1, args.warmup)):
+        for c in modes:
+            launch(c)
+    torch.cuda.synchronize()
+    t_end = time.time() + args.ramp_seconds
+    while time.time() < t_end:
+        for c in modes:
+            launch(c)
+        torch.cuda.synchronize()
+    ev = {c: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for c in modes}
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        for c in modes:
+            ev[c][s][0].record(stream)
+            launch(c)
+            ev[c][s][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    bflops = lambda c: 2.5 * flops(B, H, N, d, c)
+    step_flops = sum(bflops(c) for c in modes)
+    ms_per_step = wall * 1e3 / args.steps
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    per_mode = {}
+    for c in modes:
+        ms = np.array([a.elapsed_time(b) for a, b in ev[c]])
+        avg = float(ms.mean())
+        tf = bflops(c) / (avg * 1e-3) / 1e12
+        per_mode["causal" if c else "noncausal"] = dict(
+            call_ms_avg=round(avg, 5), call_ms_median=round(float(np.median(ms)), 5),
+            call_ms_min=round(float(ms.min()), 5), tflops=round(tf, 2), frac_of_peak=round(tf / PEAK_BF16_TFLOPS, 4))
+    dom_c = max(modes, key=lambda c: per_mode["causal" if c else "noncausal"]["call_ms_avg"])
+    dom = per_mode["causal" if dom_c else "noncausal"]
+    roofline = dict(bound="mfma", achieved=dom["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=dom["frac_of_peak"], traffic=None,
+                    kernel="fa_bwd (pre + dK/dV + dQ kernels) d=%d causal=%d" % (d, dom_c),
+                    flops_per_launch=bflops(dom_c))
+
+    cpu = None
+    if not args.no_cpu_baseline and 2.5 * flops(1, 1, N, d, max(modes)) <= 300e9:
+        import oracle
+        from inputs import bf16_bits_to_f64
+        # one whole head per oracle thread, within ~300 GFLOP of fp64 work
+        nh = min(B * H, max(1, oracle.num_threads()), int(300e9 // (2.5 * flops(1, 1, N, d, max(modes)) * len(modes))))
+        heads = [(i // H, i % H) for i in range(0, B * H, max(1, (B * H) // nh))][:nh]
+        sel = lambda a: np.stack([a[b, h] for b, h in heads])[None]
+        total_flops, total_s, parity = 0.0, 0.0, {}
+        for c in modes:
+            t0 = time.perf_counter()
+            ref = oracle.attention_bwd(sel(q_bits), sel(k_bits), sel(v_bits), sel(g_bits), scale, bool(c))
+            total_s += time.perf_counter() - t0
+            total_flops += 2.5 * flops(1, len(heads), N, d, c)
+            errs = {}
+            for name, g, r in zip(("dq", "dk", "dv"), grads[c], ref):
+                gb = sel(g.view(torch.int16).cpu().numpy().view(np.uint16))
+                e = np.abs(bf16_bits_to_f64(gb) - r)
+                errs[name] = dict(max_rel=float(e.max() / np.abs(r).max()),
+                                  rms_rel=float(np.sqrt(np.mean(e ** 2)) / np.sqrt(np.mean(r ** 2))))
+            parity["causal" if c else "noncausal"] = errs
+        cpu = dict(value=round(total_flops / total_s / 1e12, 6), unit="TFLOP/s", cores=oracle.num_threads(),
+                   kind="oracle",
+                   sample="%d whole heads of %s (b, h = %s), modes %s; fp64 backward, %.1f GFLOP in %.2fs"
+                          % (len(heads), w["name"], heads, modes, total_flops / 1e9, total_s),
+                   parity_on_sample=parity)
+
+    rec = {
+        "metric": BWD_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "%s backward %s" % (w["name"], "+".join("causal" if c else "non-causal" for c in modes)),
+                   "B": B, "H": H, "N": N, "d": d, "scale": scale, "flops_per_step": step_flops, "modes": per_mode},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -1,4 +1,4 @@
-"""MI355X (gfx950) FlashAttention-2 forward: Python binding of libfa_fwd.so.
+"""MI355X (gfx950) FlashAttention-2 forward (and backward): Python binding of libfa_fwd.so.
 
 Argument marshalling only: every step of the forward pass runs in the HIP
 library; PyTorch supplies device memory and the stream.  There is no fallback:
@@ -15,11 +15,12 @@ from .buildlib import LIB, build  # noqa: F401
 
 __all__ = ["fa_fwd", "fa_fwd_ptr", "fa_fwd_cfg", "fa_fwd_ex", "fa_fwd_ex_ptr", "fa_fwd_splitkv",
            "splitkv_workspace_bytes", "splitkv_default_splits", "FwdDesc", "FaError", "strerror",
-           "version", "default_cfg", "variants", "load_library", "EXPORTED_SYMBOLS"]
+           "version", "default_cfg", "variants", "load_library", "EXPORTED_SYMBOLS", "fa_bwd", "fa_bwd_ptr",
+           "bwd_workspace_bytes"]
 
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_cfg", "fa_fwd_ex", "fa_fwd_ex_cfg", "fa_fwd_splitkv",
                     "fa_splitkv_workspace_bytes", "fa_splitkv_default_splits", "fa_default_cfg", "fa_num_variants",
-                    "fa_variant", "fa_strerror", "fa_version")
+                    "fa_variant", "fa_strerror", "fa_version", "fa_bwd", "fa_bwd_workspace_bytes")
 
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD_DIM", 4: "FA_ERR_SCALE",
           5: "FA_ERR_ARG", 6: "FA_ERR_ALIGN", 7: "FA_ERR_ALIAS", 8: "FA_ERR_NO_DEVICE",
@@ -94,6 +95,10 @@ def load_library():
             lib.fa_strerror.restype = ctypes.c_char_p
             lib.fa_version.argtypes = []
             lib.fa_version.restype = _I
+            lib.fa_bwd_workspace_bytes.argtypes = [_I, _I, _I, _I]
+            lib.fa_bwd_workspace_bytes.restype = ctypes.c_longlong
+            lib.fa_bwd.argtypes = [_P] * 9 + [_I, _I, _I, _I, ctypes.c_float, _I, _P, ctypes.c_longlong, _P]
+            lib.fa_bwd.restype = _I
             _lib = lib
     return _lib
 
@@ -276,3 +281,58 @@ def fa_fwd_splitkv(q, k, v, scale: float | None = None, causal: bool = False, ou
     _check(int(load_library().fa_fwd_splitkv(ctypes.byref(desc), int(num_splits), _P(workspace.data_ptr()),
                                              ctypes.c_longlong(nbytes))))
     return out, lse
+
+
+def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    n = int(load_library().fa_bwd_workspace_bytes(B, H, N, d))
+    if n < 0:
+        _check(-n)
+    return n
+
+
+def fa_bwd_ptr(q: int, k: int, v: int, out: int, lse: int, dout: int, dq: int, dk: int, dv: int, B: int, H: int,
+               N: int, d: int, scale: float, causal: bool, workspace: int, workspace_bytes: int,
+               stream: int = 0) -> int:
+    """Raw-pointer call of ``fa_bwd``; returns the library's status code (does not raise)."""
+    lib = load_library()
+    return int(lib.fa_bwd(_P(q), _P(k), _P(v), _P(out), _P(lse), _P(dout), _P(dq), _P(dk), _P(dv), int(B), int(H),
+                          int(N), int(d), ctypes.c_float(scale), int(causal), _P(workspace),
+                          ctypes.c_longlong(workspace_bytes), _P(stream)))
+
+
+def fa_bwd(q, k, v, out, lse, dout, scale: float | None = None, causal: bool = False, dq=None, dk=None, dv=None,
+           workspace=None, stream=None):
+    """Attention backward on torch tensors: q, k, v, out, dout bf16 [B, H, N, d]
+    and lse fp32 [B, H, N] (the forward's outputs for the same scale and mask),
+    all contiguous on one device.  Returns ``(dq, dk, dv)``, bf16 [B, H, N, d].
+    ``workspace``: a device tensor of at least ``bwd_workspace_bytes(...)`` bytes
+    (default: allocated here through torch).  Enqueued on ``stream``; no
+    synchronisation.
+    """
+    import torch
+    if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, out, dout)):
+        raise ValueError("q, k, v, out, dout must share one [B, H, N, d] shape")
+    for t in (q, k, v, out, dout):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v, out, dout must be contiguous bfloat16 device tensors")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 tensor [B, H, N]")
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    grads = []
+    for g in (dq, dk, dv):
+        if g is None:
+            g = torch.empty_like(q)
+        if g.shape != q.shape or g.dtype != torch.bfloat16 or not g.is_contiguous():
+            raise ValueError("dq, dk, dv must be contiguous bf16 tensors shaped like q")
+        grads.append(g)
+    need = bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = fa_bwd_ptr(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                    grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(), B, H, N, d, scale, causal,
+                    workspace.data_ptr(), nbytes, _stream_handle(stream, q.device))
+    _check(st)
+    return tuple(grads)

@@ -1,4 +1,4 @@
-"""Build libfa_fwd.so (HIP, gfx950 only) in-tree with hipcc."""
+"""Build libfa_fwd.so (HIP, gfx950 only; forward and backward) in-tree with hipcc."""
 from __future__ import annotations
 
 import hashlib
@@ -20,23 +20,30 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
-def source_digest() -> str:
-    """sha256 over the kernel sources and device flags: identifies the compiled
-    kernel, so that measurements taken on one build are not reported for another."""
+def source_digest(names=("fa_fwd_kernel.hpp", "fa_fwd.hip")) -> str:
+    """sha256 over kernel sources and the device flags: identifies the compiled
+    kernels, so that measurements taken on one build are not reported for
+    another.  The default covers the forward; pass ``BWD_SOURCES`` for the
+    backward."""
     h = hashlib.sha256()
-    for name in ("fa_fwd_kernel.hpp", "fa_fwd.hip"):
+    for name in names:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     h.update(" ".join(DEVICE_FLAGS).encode())
     return h.hexdigest()
 
 
+SOURCES = ("fa_fwd.hip", "fa_bwd.hip")
+BWD_SOURCES = ("fa_fwd_kernel.hpp", "fa_bwd_kernel.hpp", "fa_bwd.hip")
+
+
 def build(verbose: bool = False, extra=()) -> str:
-    src = os.path.join(CSRC, "fa_fwd.hip")
+    """Compile the forward and backward sources into one shared library."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS, *extra,
-           "-o", tmp, src]
+           "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,0 +1,492 @@
+// FlashAttention-2 backward for gfx950 (CDNA4), hand-written HIP.
+//
+// Gradients of the exact attention O = softmax(scale * Q K^T) V with respect to
+// Q, K, V, given dO.  P is never stored: each kernel recomputes it tile by tile
+// from the log-sum-exp the forward saved ("FlashAttention and kernels",
+// gtadkapally.com, the backward-pass discussion: the per-row statistics are kept
+// so that the backward can rebuild P instead of reading an N x N matrix), and
+// follows the chain rule through the softmax:
+//
+//   P  = exp(scale * Q K^T - LSE),   dV = P^T dO,   dP = dO V^T,
+//   D  = rowsum(dO o O),             dS = P o (dP - D),
+//   dQ = scale * dS K,               dK = scale * dS^T Q.
+//
+// Three kernels, no atomics (every output element is written once, by one
+// lane, so results are deterministic):
+// * fa_bwd_pre_kernel: D per query row, and LSE * log2(e) for the exp2 form.
+// * fa_bwd_dkdv_kernel: one workgroup per key tile (32 keys per wavefront, K and
+//   V of those keys held in VGPRs); it sweeps the query tiles that see those keys,
+//   staging Q, dO, LSE and D through a double-buffered LDS ring, and accumulates
+//   dK^T and dV^T in registers.
+// * fa_bwd_dq_kernel: one workgroup per query tile (32 queries per wavefront, Q
+//   and dO in VGPRs); it sweeps the key tiles like the forward, with K and V in
+//   LDS, and accumulates dQ^T.
+// The split into a key-major and a query-major pass recomputes S and dP twice
+// (7 matrix products instead of 5) in exchange for no atomic traffic on dQ.
+//
+// MFMA mapping (v_mfma_f32_32x32x16_bf16; C lane l, register r holds row
+// 8(r/4) + 4(l/32) + r%4, column l%32):
+// * dK/dV pass: S = Q K^T and dP = dO V^T with Q (dO) rows read from LDS as the A
+//   operand and K (V) rows in VGPRs as the B operand, so a lane owns ONE key and
+//   16 queries; P and dS packed to bf16 are then already the B operand of
+//   dV^T += dO^T P and dK^T += Q^T dS, whose A operands are dO and Q read
+//   transposed from LDS (ds_read_b64_tr_b16) in the order the C layout holds the
+//   queries.  Each lane needs LSE and D of its 16 queries: four 16-byte LDS
+//   reads each per 32 queries.
+// * dQ pass: S^T = K Q^T and dP^T = V dO^T (lane = one query, as in the
+//   forward), dS^T packed to bf16 is the B operand of dQ^T += K^T dS^T, with K
+//   read transposed from LDS.
+// LDS tiles use the forward's XOR swizzle, which keeps both the row reads and
+// the transposed reads free of bank conflicts.
+#pragma once
+#include "fa_fwd_kernel.hpp"
+
+namespace fa {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// Kernel arguments of the backward.  All tensors contiguous [B, H, N, d]
+// (lse [B, H, N]); the workspace holds lse2 and dsum, [B, H, N] fp32 each.
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* out;
+  const uint16_t* dout;
+  const float* lse;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* lse2;  // LSE * log2(e)
+  float* dsum;  // D = rowsum(dO o O)
+  int BH, N, ntiles;
+  float qk_scale;  // scale * log2(e)
+  float scale;
+};
+
+// 4 bytes per lane, global -> LDS: lane l's word lands at dst + 4*l.
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rsrc, char* dst, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 4, voffset, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// A operand of 32x32x16 read transposed out of a row-major (swizzled) LDS
+// tile: rows (keys or queries) 16*step + {4g + 0..3, 8 + 4g + 0..3}, columns
+// db*32 + lane%32 -- the order in which a C fragment holds its rows.
+__device__ __forceinline__ bf16x8 read_tr(const char* base, int lo, int hi) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + lo));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + hi));
+  const u32x4 w = {__builtin_bit_cast(u32x2, a)[0], __builtin_bit_cast(u32x2, a)[1], __builtin_bit_cast(u32x2, b)[0],
+                   __builtin_bit_cast(u32x2, b)[1]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Per-lane byte offsets of read_tr inside a tile: [db][0] for the low four
+// rows, [db][1] for the high four.  In each 16-lane group (s = lane / 16), lane
+// 4r + tt supplies 4 elements of row (4g + r, +8 for the high half) starting at
+// column db*32 + 16*(s & 1) + 4*tt.
+template <int D>
+__device__ __forceinline__ void tr_offsets(int lane, int (&off)[D / 32][2]) {
+  const int g = lane >> 5, s = lane >> 4, jj = lane & 15, r = jj >> 2, tt = jj & 3;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int row = 4 * g + r + 8 * hi;
+      const int col = db * 32 + 16 * (s & 1) + 4 * tt;
+      off[db][hi] = lds_offset<D>(row, col >> 3) + ((col & 4) << 1);
+    }
+}
+
+// A C fragment's 16 values as two bf16 B operands (16 rows each): element e of
+// operand h is register 8h + e.
+__device__ __forceinline__ void pack_b(const f32x16& x, bf16x8 (&b)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[8 * h + 2 * e], x[8 * h + 2 * e + 1]);
+    b[h] = __builtin_bit_cast(bf16x8, w);
+  }
+}
+
+// Workgroup -> (head, tile).  Round-robin dispatch over the 8 XCDs is undone
+// when the head count allows, so that each XCD works through a contiguous set
+// of heads; `rank` 0 is the tile to run first (the caller maps it to its
+// longest tile when causal).
+__device__ __forceinline__ void tile_of(int i, int total, int BH, int ntiles, bool causal, int& bh, int& rank) {
+  const bool xcd = (BH % 8) == 0;
+  const int t = xcd ? (i & 7) * (total >> 3) + (i >> 3) : i;
+  if (causal) {
+    if (xcd) {
+      const int per = total >> 3, hpx = BH >> 3;
+      const int chunk = t / per, j = t - chunk * per;
+      bh = chunk * hpx + j % hpx;
+      rank = j / hpx;
+    } else {
+      bh = t % BH;
+      rank = t / BH;
+    }
+  } else {
+    bh = t / ntiles;
+    rank = t - bh * ntiles;
+  }
+}
+
+// ---- D = rowsum(dO o O) and LSE * log2(e), one row per D/8 lanes ------------
+template <int D>
+__global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const BwdParams pr) {
+  constexpr int kLanes = D / 8;  // 16 bytes of a row per lane
+  const long long rows = (long long)pr.BH * pr.N;
+  const long long r = (long long)blockIdx.x * (256 / kLanes) + threadIdx.x / kLanes;
+  const int c = (threadIdx.x % kLanes) * 8;
+  float acc = 0.f;
+  if (r < rows) {
+    const u32x4 o = *reinterpret_cast<const u32x4*>(pr.out + r * D + c);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(pr.dout + r * D + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(bf16_lo(o[e]), bf16_lo(g[e]), acc);
+      acc = fmaf(bf16_hi(o[e]), bf16_hi(g[e]), acc);
+    }
+  }
+#pragma unroll
+  for (int m = kLanes / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kLanes);
+  if (r < rows && c == 0) {
+    pr.dsum[r] = acc;
+    pr.lse2[r] = pr.lse[r] * kLog2e;
+  }
+}
+
+// ---- dK, dV: one workgroup per WAVES*32 keys ---------------------------------
+template <int D, bool CAUSAL, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams pr) {
+  constexpr int BQ = 64;                          // queries per staged tile
+  constexpr int kBK = WAVES * 32;                 // keys per workgroup
+  constexpr int kTileBytes = BQ * D * 2;          // one Q or dO tile
+  constexpr int kBlocks = kTileBytes / 1024;      // 1 KB direct-load blocks per tile
+  constexpr int kBlocksPerWave = (kBlocks + WAVES - 1) / WAVES;
+  constexpr int kStageBytes = 2 * kTileBytes + 2 * BQ * 4;  // Q, dO, lse2, dsum
+  static_assert(WAVES >= 2 && kBK % BQ == 0, "tile shape");
+  static_assert(2 * kStageBytes <= 160 * 1024, "LDS budget of one CU");
+  __shared__ __attribute__((aligned(1024))) char lds0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds1[kStageBytes];
+
+  const int N = pr.N;
+  const float qk_scale = pr.qk_scale;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, lr = lane & 31;
+
+  int bh, kt;
+  tile_of((int)blockIdx.x, (int)gridDim.x, pr.BH, pr.ntiles, CAUSAL, bh, kt);
+  const long long hoff = (long long)bh * N * D;
+  const uint32_t tbytes = (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(pr.q + hoff, tbytes);
+  const __amdgpu_buffer_rsrc_t drs = make_rsrc(pr.dout + hoff, tbytes);
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(pr.lse2 + (long long)bh * N, (uint32_t)N * 4);
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(pr.dsum + (long long)bh * N, (uint32_t)N * 4);
+  const int k0 = kt * kBK;
+  const int kw = k0 + wave * 32;  // first key of this wavefront
+
+  // ---- this wavefront's K and V rows -> VGPRs (rows >= N read 0) -------------
+  bf16x8 kreg[D / 16], vreg[D / 16];
+  {
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(pr.k + hoff, tbytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(pr.v + hoff, tbytes);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const uint32_t off = ((kw + lr) * D + ks * 16 + g * 8) * 2;
+      kreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+      vreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
+    }
+  }
+
+  uint32_t dma[kBlocksPerWave];
+#pragma unroll
+  for (int n = 0; n < kBlocksPerWave; ++n) {
+    const int p = (wave + WAVES * n) * 64 + lane;
+    const int row = p / (D / 8), pos = p % (D / 8);
+    dma[n] = row * D * 2 + ((pos ^ swz<D>(row)) << 4);
+  }
+  int roff[D / 16];  // row reads: row lr, chunk 2*ks + g
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) roff[ks] = lds_offset<D>(lr, 2 * ks + g);
+  int toff[D / 32][2];
+  tr_offsets<D>(lane, toff);
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dk[db] = dv[db] = f32x16{};
+
+  // Causal: queries before k0 see none of these keys.
+  const int qbeg = CAUSAL ? k0 : 0;
+  const int ntiles = (N - qbeg + BQ - 1) / BQ;
+
+  auto issue_tile = [&](int j, int stage) {
+    const int qs = qbeg + j * BQ;
+    char* st = stage ? lds1 : lds0;
+    const uint32_t gq = (uint32_t)qs * D * 2;
+#pragma unroll
+    for (int n = 0; n < kBlocksPerWave; ++n) {
+      const int b = wave + WAVES * n;
+      if (kBlocks % WAVES == 0 || b < kBlocks) {
+        dma16(qrs, st + b * 1024, dma[n] + gq);
+        dma16(drs, st + kTileBytes + b * 1024, dma[n] + gq);
+      }
+    }
+    if (wave == 0) dma4(lrs, st + 2 * kTileBytes, (uint32_t)(qs + lane) * 4);
+    if (wave == 1) dma4(srs, st + 2 * kTileBytes + BQ * 4, (uint32_t)(qs + lane) * 4);
+  };
+
+  auto compute_tile = [&](const char* st, int qs) {
+    const char* qst = st;
+    const char* dst = st + kTileBytes;
+    const float* lst = reinterpret_cast<const float*>(st + 2 * kTileBytes);
+    const float* sst = lst + BQ;
+#pragma unroll
+    for (int qb = 0; qb < BQ / 32; ++qb) {
+      const int qbase = qs + qb * 32;
+      // Multiples of 32 both: either every query of the block precedes every
+      // key of the wavefront, or the block is the diagonal one, or it follows.
+      if (CAUSAL && qbase < kw) continue;
+      const bool diag = CAUSAL && qbase == kw;
+      // ---- S = Q K^T, dP = dO V^T (lane = key, 16 queries) ------------------
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(qst + qb * 32 * (D * 2) + roff[ks]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[ks], s, 0, 0, 0);
+      }
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(dst + qb * 32 * (D * 2) + roff[ks]);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vreg[ks], dp, 0, 0, 0);
+      }
+      // ---- P and dS -----------------------------------------------------------
+      f32x4 L[4], Dq[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        L[j] = *reinterpret_cast<const f32x4*>(lst + qb * 32 + 8 * j + 4 * g);
+        Dq[j] = *reinterpret_cast<const f32x4*>(sst + qb * 32 + 8 * j + 4 * g);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(fmaf(s[r], qk_scale, -L[r >> 2][r & 3]));
+        if (diag && (lr > 8 * (r >> 2) + 4 * g + (r & 3))) p = 0.f;  // key > query
+        s[r] = p;
+        dp[r] = p * (dp[r] - Dq[r >> 2][r & 3]);
+      }
+      bf16x8 pb[2], db16[2];
+      pack_b(s, pb);
+      pack_b(dp, db16);
+      // ---- dV^T += dO^T P, dK^T += Q^T dS --------------------------------------
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int rowoff = (2 * qb + h) * 16 * (D * 2);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(dst + rowoff, toff[db][0], toff[db][1]), pb[h],
+                                                           dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(qst + rowoff, toff[db][0], toff[db][1]), db16[h],
+                                                           dk[db], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  auto step = [&](int j, int stage) {
+    if (j + 1 < ntiles) issue_tile(j + 1, stage ^ 1);
+    compute_tile(stage ? lds1 : lds0, qbeg + j * BQ);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads landed
+    __syncthreads();                     // ... every wave's, and this stage is free
+  };
+
+  issue_tile(0, 0);  // ntiles >= 1: k0 < N
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  int j = 0;
+  for (; j + 1 < ntiles; j += 2) {
+    step(j, 0);
+    step(j + 1, 1);
+  }
+  if (j < ntiles) step(j, 0);
+
+  // ---- epilogue: dK = scale * dK^T^T, dV -> bf16 --------------------------------
+  const int key = kw + lr;
+  if (key < N) {
+    uint16_t* krow = pr.dk + hoff + (long long)key * D;
+    uint16_t* vrow = pr.dv + hoff + (long long)key * D;
+    const float sc = pr.scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        u32x2 a, b;
+        a[0] = pack_bf16x2(dk[db][4 * rr + 0] * sc, dk[db][4 * rr + 1] * sc);
+        a[1] = pack_bf16x2(dk[db][4 * rr + 2] * sc, dk[db][4 * rr + 3] * sc);
+        b[0] = pack_bf16x2(dv[db][4 * rr + 0], dv[db][4 * rr + 1]);
+        b[1] = pack_bf16x2(dv[db][4 * rr + 2], dv[db][4 * rr + 3]);
+        *reinterpret_cast<u32x2*>(krow + db * 32 + 8 * rr + 4 * g) = a;
+        *reinterpret_cast<u32x2*>(vrow + db * 32 + 8 * rr + 4 * g) = b;
+      }
+  }
+}
+
+// ---- dQ: one workgroup per WAVES*32 queries, key tiles of BK -----------------
+template <int D, bool CAUSAL, int WAVES, int BK>
+__global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams pr) {
+  constexpr int kBQ = WAVES * 32;
+  constexpr int kTileBytes = BK * D * 2;  // one K or V tile
+  constexpr int kBlocks = kTileBytes / 1024;
+  constexpr int kBlocksPerWave = (kBlocks + WAVES - 1) / WAVES;
+  constexpr int kStageBytes = 2 * kTileBytes;  // K then V
+  static_assert(BK % 32 == 0 && kTileBytes % 1024 == 0, "key tile");
+  static_assert(2 * kStageBytes <= 160 * 1024, "LDS budget of one CU");
+  __shared__ __attribute__((aligned(1024))) char lds0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds1[kStageBytes];
+
+  const int N = pr.N, nqt = pr.ntiles;
+  const float qk_scale = pr.qk_scale;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, lr = lane & 31;
+
+  int bh, rank;
+  tile_of((int)blockIdx.x, (int)gridDim.x, pr.BH, nqt, CAUSAL, bh, rank);
+  const int qt = CAUSAL ? nqt - 1 - rank : rank;  // causal: longest (last) query tile first
+  const long long hoff = (long long)bh * N * D;
+  const uint32_t tbytes = (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(pr.k + hoff, tbytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(pr.v + hoff, tbytes);
+  const int q0 = qt * kBQ;
+  const int qw = q0 + wave * 32;
+  const int query = qw + lr;
+
+  // ---- Q and dO rows -> VGPRs (B operands), LSE and D of this lane's query ----
+  bf16x8 qreg[D / 16], doreg[D / 16];
+  {
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(pr.q + hoff, tbytes);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(pr.dout + hoff, tbytes);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const uint32_t off = (query * D + ks * 16 + g * 8) * 2;
+      qreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
+      doreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(drs, off, 0, 0));
+    }
+  }
+  float l2 = 0.f, dd = 0.f;
+  if (query < N) {
+    l2 = pr.lse2[(long long)bh * N + query];
+    dd = pr.dsum[(long long)bh * N + query];
+  }
+
+  uint32_t dma[kBlocksPerWave];
+#pragma unroll
+  for (int n = 0; n < kBlocksPerWave; ++n) {
+    const int p = (wave + WAVES * n) * 64 + lane;
+    const int row = p / (D / 8), pos = p % (D / 8);
+    dma[n] = row * D * 2 + ((pos ^ swz<D>(row)) << 4);
+  }
+  int roff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) roff[ks] = lds_offset<D>(lr, 2 * ks + g);
+  int toff[D / 32][2];
+  tr_offsets<D>(lane, toff);
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
+
+  const int kend = CAUSAL ? min(q0 + kBQ, N) : N;
+  const int ntiles = (kend + BK - 1) / BK;
+
+  auto issue_tile = [&](int j, int stage) {
+    const uint32_t gk = (uint32_t)(j * BK) * D * 2;
+    char* st = stage ? lds1 : lds0;
+#pragma unroll
+    for (int n = 0; n < kBlocksPerWave; ++n) {
+      const int b = wave + WAVES * n;
+      if (kBlocks % WAVES == 0 || b < kBlocks) {
+        dma16(krs, st + b * 1024, dma[n] + gk);
+        dma16(vrs, st + kTileBytes + b * 1024, dma[n] + gk);
+      }
+    }
+  };
+
+  auto compute_tile = [&](const char* kst, int k0, bool masked) {
+    const char* vst = kst + kTileBytes;
+    bf16x8 dsb[BK / 16];
+#pragma unroll
+    for (int kb = 0; kb < BK / 32; ++kb) {
+      // ---- S^T = K Q^T, dP^T = V dO^T (lane = query, 16 keys) ------------------
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kst + kb * 32 * (D * 2) + roff[ks]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s, 0, 0, 0);
+      }
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vst + kb * 32 * (D * 2) + roff[ks]);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, doreg[ks], dp, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(fmaf(s[r], qk_scale, -l2));
+        if (masked) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if ((CAUSAL && key > query) || key >= N) p = 0.f;
+        }
+        dp[r] = p * (dp[r] - dd);
+      }
+      bf16x8 b2[2];
+      pack_b(dp, b2);
+      dsb[2 * kb] = b2[0];
+      dsb[2 * kb + 1] = b2[1];
+    }
+    // ---- dQ^T += K^T dS^T ---------------------------------------------------------
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(kst + kk * 16 * (D * 2), toff[db][0], toff[db][1]),
+                                                         dsb[kk], dq[db], 0, 0, 0);
+  };
+
+  auto step = [&](int j, int stage) {
+    if (j + 1 < ntiles) issue_tile(j + 1, stage ^ 1);
+    const int k0 = j * BK;
+    const bool skip = CAUSAL && (k0 > qw + 31);
+    const bool masked = (CAUSAL && (k0 + BK - 1 > qw)) || (k0 + BK > N);
+    if (!skip) compute_tile(stage ? lds1 : lds0, k0, masked);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  };
+
+  issue_tile(0, 0);  // ntiles >= 1: q0 < N
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  int j = 0;
+  for (; j + 1 < ntiles; j += 2) {
+    step(j, 0);
+    step(j + 1, 1);
+  }
+  if (j < ntiles) step(j, 0);
+
+  if (query < N) {
+    uint16_t* row = pr.dq + hoff + (long long)query * D;
+    const float sc = pr.scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        u32x2 w;
+        w[0] = pack_bf16x2(dq[db][4 * rr + 0] * sc, dq[db][4 * rr + 1] * sc);
+        w[1] = pack_bf16x2(dq[db][4 * rr + 2] * sc, dq[db][4 * rr + 3] * sc);
+        *reinterpret_cast<u32x2*>(row + db * 32 + 8 * rr + 4 * g) = w;
+      }
+  }
+}
+
+}  // namespace fa

@@ -38,7 +38,8 @@ SEED_BASE = 0xFA2F0000
 
 
 def workload_seed(config: int, tensor: int) -> int:
-    """Seed of tensor ``tensor`` (0 = Q, 1 = K, 2 = V) of workload number ``config``."""
+    """Seed of tensor ``tensor`` of workload number ``config``: 0 = Q, 1 = K, 2 = V,
+    3 = the row sample of the CPU baseline, 4 = the upstream gradient dO."""
     return SEED_BASE + 16 * int(config) + int(tensor)
 
 

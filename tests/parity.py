@@ -56,3 +56,28 @@ def compare(o_gpu_bits, lse_gpu, o_ref, lse_ref, rows=None, label=""):
 
 def fp32_scale(d: int) -> float:
     return float(np.float32(1.0 / math.sqrt(d)))
+
+
+# Backward: each gradient tensor is compared as a whole against the fp64 oracle,
+# relative to its own scale (gradients have no fixed magnitude):
+# max |dG| <= GRAD_MAX_REL * max |G| and rms(dG) <= GRAD_RMS_REL * rms(G).
+# With u = 2^-8 (bf16 unit roundoff), rounding the outputs alone gives errors up
+# to u |G| with rms about u / sqrt(3) ~ 2.3e-3 of rms(G); the bf16 operands P and
+# dS and the bf16 O inside D add less than that again.  Bounds: 2.5 u and 1.8 u/sqrt(3).
+GRAD_MAX_REL = 1e-2
+GRAD_RMS_REL = 4e-3
+
+
+def compare_grad(g_gpu_bits, g_ref, label=""):
+    g = bf16_bits_to_f64(np.asarray(g_gpu_bits)).reshape(g_ref.shape)
+    err = np.abs(g - g_ref)
+    scale_max = max(float(np.abs(g_ref).max()), 1e-30)
+    scale_rms = max(float(np.sqrt(np.mean(g_ref ** 2))), 1e-30)
+    s = dict(max_rel=float(err.max()) / scale_max, rms_rel=float(np.sqrt(np.mean(err ** 2))) / scale_rms,
+             ref_max=scale_max, finite=bool(np.all(np.isfinite(g))))
+    print("[parity] %s max|dG|/max|G|=%.3e rms(dG)/rms(G)=%.3e max|G|=%.3e"
+          % (label, s["max_rel"], s["rms_rel"], s["ref_max"]), file=sys.stderr, flush=True)
+    assert s["finite"], "non-finite gradient"
+    assert s["max_rel"] <= GRAD_MAX_REL, s
+    assert s["rms_rel"] <= GRAD_RMS_REL, s
+    return s

@@ -9,7 +9,7 @@ import pytest
 import flashattention_forward_fa2_amd as fa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "fa_fwd.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("fa_fwd.h", "fa_bwd.h")]
 
 
 @pytest.fixture(scope="module")
@@ -20,7 +20,7 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"^(?:int|long long|const char \*)\s*\*?\s*(fa_\w+)\s*\(", text, re.M)))
 
 
@@ -219,3 +219,49 @@ def test_splitkv_valid_call_reaches_the_device_check(lib):
         pytest.skip("a GPU is present")
     d = desc(Nq=1, Nk=4096)
     assert lib.fa_fwd_splitkv(ctypes.byref(d), 0, ctypes.c_void_p(WS), ctypes.c_longlong(1 << 30)) == 8
+
+
+# ---------------------------------------------------------------- backward
+
+def bwd_call(**kw):
+    a = dict(q=FAKE, k=2 * FAKE, v=3 * FAKE, out=4 * FAKE, lse=5 * FAKE, dout=6 * FAKE, dq=7 * FAKE, dk=8 * FAKE,
+             dv=9 * FAKE, B=1, H=2, N=64, d=64, scale=0.125, causal=0, ws=WS, nbytes=1 << 30)
+    a.update(kw)
+    return fa.fa_bwd_ptr(a["q"], a["k"], a["v"], a["out"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"], a["B"],
+                         a["H"], a["N"], a["d"], a["scale"], a["causal"], a["ws"], a["nbytes"], 0)
+
+
+def test_bwd_header_compiles_as_c99(tmp_path):
+    src = tmp_path / "b.c"
+    src.write_text("#include \"fa_bwd.h\"\nint main(void){return fa_bwd_workspace_bytes(1,1,1,64) > 0 ? 0 : 1;}\n")
+    assert os.system("gcc -std=c99 -fsyntax-only -I %s %s" % (os.path.join(ROOT, "include"), src)) == 0
+
+
+def test_bwd_workspace_bytes(lib):
+    assert fa.bwd_workspace_bytes(4, 8, 4096, 64) == 8 * 4 * 8 * 4096
+    assert fa.bwd_workspace_bytes(1, 1, 1, 128) == 8
+    assert lib.fa_bwd_workspace_bytes(1, 1, 1, 96) == -3
+    assert lib.fa_bwd_workspace_bytes(0, 1, 1, 64) == -2
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(dout=0), 1), (dict(dv=0), 1), (dict(ws=0), 1), (dict(lse=0), 1),
+    (dict(B=0), 2), (dict(N=1 << 24, d=128), 2), (dict(d=32), 3),
+    (dict(scale=0.0), 4), (dict(scale=float("nan")), 4), (dict(causal=2), 5),
+    (dict(dout=6 * FAKE + 8), 6), (dict(dk=8 * FAKE + 2), 6), (dict(lse=5 * FAKE + 1), 6),
+    (dict(ws=WS + 64), 12), (dict(nbytes=8 * 2 * 64 - 1), 12),
+    (dict(dq=FAKE), 7),                 # dq overwrites q
+    (dict(dk=7 * FAKE + 64), 7),        # dk overlaps dq
+    (dict(dv=5 * FAKE), 7),             # dv overlaps lse
+    (dict(ws=6 * FAKE), 7),             # the workspace overlaps dout
+])
+def test_bwd_argument_errors(lib, kw, code):
+    assert bwd_call(**kw) == code
+
+
+def test_bwd_valid_call_reaches_the_device_check(lib):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert bwd_call() == 8
+    assert bwd_call(q=FAKE, k=FAKE, v=FAKE, nbytes=8 * 2 * 64) == 8  # inputs may alias; exact workspace size
