@@ -14,9 +14,21 @@
 
 namespace {
 
-constexpr int kDkdvWaves = 4;  // 128 keys per dK/dV workgroup
+// dK/dV workgroup: d = 64, 4 wavefronts with K and V in VGPRs (two workgroups
+// per CU); d = 128, 8 wavefronts with V resident in LDS (one workgroup per CU,
+// two wavefronts per SIMD either way).
+#ifndef FA_DKDV_VLDS
+#define FA_DKDV_VLDS 1
+#endif
+template <int D>
+constexpr bool kDkdvVlds = D == 128 && FA_DKDV_VLDS;
+template <int D>
+constexpr int kDkdvWaves = kDkdvVlds<D> ? 8 : 4;
 constexpr int kDqWaves = 4;    // 128 queries per dQ workgroup
-constexpr int kDqBK = 64;      // key tile of the dQ sweep
+// Key tile of the dQ sweep: 32 at d = 128 keeps the kernel within 256 registers
+// (two wavefronts per SIMD), 64 at d = 64.
+template <int D>
+constexpr int kDqBK = D == 128 ? 32 : 64;
 
 bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
@@ -94,15 +106,15 @@ hipError_t launch(const fa::BwdParams& p0, hipStream_t stream) {
   hipLaunchKernelGGL((fa::fa_bwd_pre_kernel<D>), dim3((unsigned)pre_blocks), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int kBK = kDkdvWaves * 32;
+  constexpr int kBK = kDkdvWaves<D> * 32;
   p.ntiles = (p.N + kBK - 1) / kBK;
-  hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<D, CAUSAL, kDkdvWaves>), dim3((unsigned)(p.BH * p.ntiles)),
-                     dim3(kDkdvWaves * 64), 0, stream, p);
+  hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<D, CAUSAL, kDkdvWaves<D>, kDkdvVlds<D>>),
+                     dim3((unsigned)(p.BH * p.ntiles)), dim3(kDkdvWaves<D> * 64), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int kBQ = kDqWaves * 32;
   p.ntiles = (p.N + kBQ - 1) / kBQ;
-  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<D, CAUSAL, kDqWaves, kDqBK>), dim3((unsigned)(p.BH * p.ntiles)),
+  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<D, CAUSAL, kDqWaves, kDqBK<D>>), dim3((unsigned)(p.BH * p.ntiles)),
                      dim3(kDqWaves * 64), 0, stream, p);
   return hipGetLastError();
 }

@@ -2,10 +2,9 @@
 //
 // Gradients of the exact attention O = softmax(scale * Q K^T) V with respect to
 // Q, K, V, given dO.  P is never stored: each kernel recomputes it tile by tile
-// from the log-sum-exp the forward saved ("FlashAttention and kernels",
-// gtadkapally.com, the backward-pass discussion: the per-row statistics are kept
-// so that the backward can rebuild P instead of reading an N x N matrix), and
-// follows the chain rule through the softmax:
+// from the log-sum-exp the forward saved, and follows the chain rule through
+// the softmax ("FlashAttention and kernels", gtadkapally.com, section "The
+// backward pass: recompute instead of remember"):
 //
 //   P  = exp(scale * Q K^T - LSE),   dV = P^T dO,   dP = dO V^T,
 //   D  = rowsum(dO o O),             dS = P o (dP - D),
@@ -161,7 +160,11 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const BwdParams pr) {
 }
 
 // ---- dK, dV: one workgroup per WAVES*32 keys ---------------------------------
-template <int D, bool CAUSAL, int WAVES>
+// VLDS = false: each wavefront holds its 32 K and V rows in VGPRs.  VLDS = true
+// (d = 128): V rows stay in LDS for the whole sweep and are read as the B
+// operand of dP = dO V^T, which frees the 32 VGPRs that let two wavefronts share
+// a SIMD.
+template <int D, bool CAUSAL, int WAVES, bool VLDS>
 __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams pr) {
   constexpr int BQ = 64;                          // queries per staged tile
   constexpr int kBK = WAVES * 32;                 // keys per workgroup
@@ -169,10 +172,12 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
   constexpr int kBlocks = kTileBytes / 1024;      // 1 KB direct-load blocks per tile
   constexpr int kBlocksPerWave = (kBlocks + WAVES - 1) / WAVES;
   constexpr int kStageBytes = 2 * kTileBytes + 2 * BQ * 4;  // Q, dO, lse2, dsum
+  constexpr int kVBytes = VLDS ? kBK * D * 2 : 1024;        // resident V rows
   static_assert(WAVES >= 2 && kBK % BQ == 0, "tile shape");
-  static_assert(2 * kStageBytes <= 160 * 1024, "LDS budget of one CU");
+  static_assert(2 * kStageBytes + (VLDS ? kVBytes : 0) <= 160 * 1024, "LDS budget of one CU");
   __shared__ __attribute__((aligned(1024))) char lds0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char lds1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char vlds[kVBytes];
 
   const int N = pr.N;
   const float qk_scale = pr.qk_scale;
@@ -190,19 +195,6 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
   const int k0 = kt * kBK;
   const int kw = k0 + wave * 32;  // first key of this wavefront
 
-  // ---- this wavefront's K and V rows -> VGPRs (rows >= N read 0) -------------
-  bf16x8 kreg[D / 16], vreg[D / 16];
-  {
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(pr.k + hoff, tbytes);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(pr.v + hoff, tbytes);
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const uint32_t off = ((kw + lr) * D + ks * 16 + g * 8) * 2;
-      kreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
-      vreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
-    }
-  }
-
   uint32_t dma[kBlocksPerWave];
 #pragma unroll
   for (int n = 0; n < kBlocksPerWave; ++n) {
@@ -215,6 +207,33 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
   for (int ks = 0; ks < D / 16; ++ks) roff[ks] = lds_offset<D>(lr, 2 * ks + g);
   int toff[D / 32][2];
   tr_offsets<D>(lane, toff);
+
+  // ---- this wavefront's K rows (and V rows, or the workgroup's V -> LDS) -------
+  bf16x8 kreg[D / 16], vreg[VLDS ? 1 : D / 16];
+  {
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(pr.k + hoff, tbytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(pr.v + hoff, tbytes);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const uint32_t off = ((kw + lr) * D + ks * 16 + g * 8) * 2;
+      kreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+      if constexpr (!VLDS)
+        vreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
+    }
+    if constexpr (VLDS) {
+      // kBK rows of V, swizzled like a tile; rows >= N read 0.  Waited for with
+      // the first Q / dO tile.
+      constexpr int kVBlocksPerWave = kVBytes / 1024 / WAVES;
+      const uint32_t gv = (uint32_t)k0 * D * 2;
+#pragma unroll
+      for (int n = 0; n < kVBlocksPerWave; ++n) {
+        const int p = (wave + WAVES * n) * 64 + lane;
+        const int row = p / (D / 8), pos = p % (D / 8);
+        dma16(vrs, vlds + (wave + WAVES * n) * 1024, gv + row * D * 2 + ((pos ^ swz<D>(row)) << 4));
+      }
+    }
+  }
+  const char* vrow = vlds + wave * 32 * (D * 2);  // this wavefront's V rows
 
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
@@ -262,21 +281,26 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(dst + qb * 32 * (D * 2) + roff[ks]);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vreg[ks], dp, 0, 0, 0);
+        bf16x8 b;
+        if constexpr (VLDS)
+          b = *reinterpret_cast<const bf16x8*>(vrow + roff[ks]);
+        else
+          b = vreg[ks];
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, dp, 0, 0, 0);
       }
       // ---- P and dS -----------------------------------------------------------
-      f32x4 L[4], Dq[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        L[j] = *reinterpret_cast<const f32x4*>(lst + qb * 32 + 8 * j + 4 * g);
-        Dq[j] = *reinterpret_cast<const f32x4*>(sst + qb * 32 + 8 * j + 4 * g);
-      }
+        const f32x4 L = *reinterpret_cast<const f32x4*>(lst + qb * 32 + 8 * j + 4 * g);
+        const f32x4 Dq = *reinterpret_cast<const f32x4*>(sst + qb * 32 + 8 * j + 4 * g);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(fmaf(s[r], qk_scale, -L[r >> 2][r & 3]));
-        if (diag && (lr > 8 * (r >> 2) + 4 * g + (r & 3))) p = 0.f;  // key > query
-        s[r] = p;
-        dp[r] = p * (dp[r] - Dq[r >> 2][r & 3]);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * j + e;
+          float p = __builtin_amdgcn_exp2f(fmaf(s[r], qk_scale, -L[e]));
+          if (diag && (lr > 8 * j + 4 * g + e)) p = 0.f;  // key > query
+          s[r] = p;
+          dp[r] = p * (dp[r] - Dq[e]);
+        }
       }
       bf16x8 pb[2], db16[2];
       pack_b(s, pb);
@@ -293,6 +317,9 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
                                                            dk[db], 0, 0, 0);
         }
       }
+      // At 256 VGPRs (d = 128) two query blocks in flight do not fit: keep the
+      // scheduler from overlapping them.
+      if constexpr (VLDS) __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -313,11 +340,11 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
   }
   if (j < ntiles) step(j, 0);
 
-  // ---- epilogue: dK = scale * dK^T^T, dV -> bf16 --------------------------------
+  // ---- epilogue: dK = scale * (dK^T)^T, dV -> bf16 --------------------------------
   const int key = kw + lr;
   if (key < N) {
     uint16_t* krow = pr.dk + hoff + (long long)key * D;
-    uint16_t* vrow = pr.dv + hoff + (long long)key * D;
+    uint16_t* vout = pr.dv + hoff + (long long)key * D;
     const float sc = pr.scale;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -329,7 +356,7 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
         b[0] = pack_bf16x2(dv[db][4 * rr + 0], dv[db][4 * rr + 1]);
         b[1] = pack_bf16x2(dv[db][4 * rr + 2], dv[db][4 * rr + 3]);
         *reinterpret_cast<u32x2*>(krow + db * 32 + 8 * rr + 4 * g) = a;
-        *reinterpret_cast<u32x2*>(vrow + db * 32 + 8 * rr + 4 * g) = b;
+        *reinterpret_cast<u32x2*>(vout + db * 32 + 8 * rr + 4 * g) = b;
       }
   }
 }

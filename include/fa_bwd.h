@@ -14,8 +14,9 @@
  * This is the chain rule through the softmax that FlashAttention's backward
  * applies, rebuilding P tile by tile from the saved per-row statistic instead
  * of storing the N x N matrix ("FlashAttention and kernels", gtadkapally.com,
- * the backward-pass discussion; D is the per-row correction term of the
- * softmax Jacobian).  No atomics are used; results are deterministic.
+ * section "The backward pass: recompute instead of remember"; D is the per-row
+ * correction term of the softmax Jacobian).  No atomics are used; results are
+ * deterministic.
  */
 #ifndef FA_BWD_H
 #define FA_BWD_H
