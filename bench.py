@@ -324,7 +324,7 @@ def main_bwd(args):
     dom_c = max(modes, key=lambda c: per_mode["causal" if c else "noncausal"]["call_ms_avg"])
     dom = per_mode["causal" if dom_c else "noncausal"]
     roofline = dict(bound="mfma", achieved=dom["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=dom["frac_of_peak"], traffic=None,
+                    frac=dom["frac_of_peak"], traffic=measured_traffic_bwd(B, H, N, d, dom_c),
                     kernel="fa_bwd (pre + dK/dV + dQ kernels) d=%d causal=%d" % (d, dom_c),
                     flops_per_launch=bflops(dom_c))
 
@@ -398,6 +398,22 @@ def measured_traffic(B, H, N, d, causal):
     if not digest or digest.group(1) != source_digest():
         return None
     m = re.search(r"traffic-bytes-per-launch d%d %s B%dH%dN%d: (\d+)"
+                  % (d, "causal" if causal else "noncausal", B, H, N), text)
+    return int(m.group(1)) if m else None
+
+
+def measured_traffic_bwd(B, H, N, d, causal):
+    """HBM bytes of one fa_bwd call (its three kernels) from the committed counter
+    summary, or None when there is none for this shape or the sources changed."""
+    from flashattention_forward_fa2_amd.buildlib import BWD_SOURCES, source_digest
+    path = os.path.join(ROOT, "profiles", "fa_bwd_d%d_B%dH%dN%d_hbm_traffic.md" % (d, B, H, N))
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    digest = re.search(r"kernel-source-sha256: ([0-9a-f]{64})", text)
+    if not digest or digest.group(1) != source_digest(BWD_SOURCES):
+        return None
+    m = re.search(r"traffic-bytes-per-call d%d %s B%dH%dN%d: (\d+)"
                   % (d, "causal" if causal else "noncausal", B, H, N), text)
     return int(m.group(1)) if m else None
 

@@ -25,10 +25,10 @@ constexpr bool kDkdvVlds = D == 128 && FA_DKDV_VLDS;
 template <int D>
 constexpr int kDkdvWaves = kDkdvVlds<D> ? 8 : 4;
 constexpr int kDqWaves = 4;    // 128 queries per dQ workgroup
-// Key tile of the dQ sweep: 32 at d = 128 keeps the kernel within 256 registers
-// (two wavefronts per SIMD), 64 at d = 64.
+// Key tile of the dQ sweep: 32 keys (at d = 128 this keeps the kernel within
+// 256 registers, two wavefronts per SIMD; at d = 64, three).
 template <int D>
-constexpr int kDqBK = D == 128 ? 32 : 64;
+constexpr int kDqBK = 32;
 
 bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
