@@ -99,6 +99,34 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
+def f64_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp64 values once, to nearest-even, to IEEE fp16; returns the uint16 bits."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of fp16 bit patterns to fp64."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def bits_to_f64(bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    return f16_bits_to_f64(bits) if dtype == "f16" else bf16_bits_to_f64(bits)
+
+
+def normal_f16(seed: int, count: int, sigma: float = 1.0) -> np.ndarray:
+    """``count`` i.i.d. N(0, sigma^2) values rounded to fp16 (uint16 bits); the
+    same normals as ``normal_bf16`` for the same seed."""
+    out = np.empty(count, dtype=np.uint16)
+    for s in range(0, count, _CHUNK):
+        n = min(_CHUNK, count - s)
+        out[s:s + n] = f64_to_f16_bits(_normals_f64(seed, s, n) * float(sigma))
+    return out
+
+
+def normal_bits(seed: int, count: int, sigma: float = 1.0, dtype: str = "bf16") -> np.ndarray:
+    return normal_f16(seed, count, sigma) if dtype == "f16" else normal_bf16(seed, count, sigma)
+
+
 def normal_bf16(seed: int, count: int, sigma: float = 1.0, threads: int | None = None) -> np.ndarray:
     """``count`` i.i.d. N(0, sigma^2) values rounded to bfloat16 (uint16 bits)."""
     out = np.empty(count, dtype=np.uint16)
@@ -155,12 +183,14 @@ def make_qkv(config: int, B: int | None = None, H: int | None = None, N: int | N
     return q, k, v
 
 
-def random_qkv(seed: int, B: int, H: int, N: int, d: int, sigma_qk: float = 1.0, sigma_v: float = 1.0):
-    """Q, K, V for an arbitrary seed (three consecutive sub-seeds)."""
+def random_qkv(seed: int, B: int, H: int, N: int, d: int, sigma_qk: float = 1.0, sigma_v: float = 1.0,
+               dtype: str = "bf16"):
+    """Q, K, V for an arbitrary seed (three consecutive sub-seeds), as bfloat16
+    or fp16 bit patterns."""
     count = B * H * N * d
-    q = normal_bf16(seed * 3 + 0, count, sigma_qk).reshape(B, H, N, d)
-    k = normal_bf16(seed * 3 + 1, count, sigma_qk).reshape(B, H, N, d)
-    v = normal_bf16(seed * 3 + 2, count, sigma_v).reshape(B, H, N, d)
+    q = normal_bits(seed * 3 + 0, count, sigma_qk, dtype).reshape(B, H, N, d)
+    k = normal_bits(seed * 3 + 1, count, sigma_qk, dtype).reshape(B, H, N, d)
+    v = normal_bits(seed * 3 + 2, count, sigma_v, dtype).reshape(B, H, N, d)
     return q, k, v
 
 

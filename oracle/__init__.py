@@ -56,6 +56,10 @@ def _load():
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                 ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
                 ctypes.c_void_p, ctypes.c_void_p]
+            lib.oracle_attention_rows_dt.restype = ctypes.c_int
+            lib.oracle_attention_rows_dt.argtypes = lib.oracle_attention_rows_qk.argtypes + [ctypes.c_int]
+            lib.oracle_element_to_f64.restype = ctypes.c_double
+            lib.oracle_element_to_f64.argtypes = [ctypes.c_uint16, ctypes.c_int]
             lib.oracle_attention_bwd.restype = ctypes.c_int
             lib.oracle_attention_bwd.argtypes = [
                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -71,11 +75,19 @@ def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
 
-def attention_rows(q, k, v, scale: float, causal: bool, rows=None):
+DTYPES = {"bf16": 0, "f16": 1}
+
+
+def element_to_f64(bits: int, dtype: str = "bf16") -> float:
+    """The oracle's own widening of one 16-bit pattern (exposed for pinning)."""
+    return float(_load().oracle_element_to_f64(int(bits), DTYPES[dtype]))
+
+
+def attention_rows(q, k, v, scale: float, causal: bool, rows=None, dtype: str = "bf16"):
     """Exact attention for selected query rows, in fp64.
 
-    ``q``: uint16 bfloat16 bit array [B, H, Nq, d]; ``k, v``: [B, H, Nk, d]
-    (contiguous).  Causal masking is top-left (key j visible to query i iff
+    ``q``: uint16 bit array [B, H, Nq, d] of bfloat16 (``dtype="bf16"``) or fp16
+    (``dtype="f16"``) values; ``k, v``: [B, H, Nk, d] (contiguous).  Causal masking is top-left (key j visible to query i iff
     j <= i).  ``scale``: the softmax scale (a Python float; pass the fp32 value
     the GPU receives, widened).  ``rows``: flat query row ids
     ``(b*H + h)*Nq + i``; ``None`` means every row.  Returns
@@ -93,11 +105,11 @@ def attention_rows(q, k, v, scale: float, causal: bool, rows=None):
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     out = np.empty((rows.size, d), dtype=np.float64)
     lse = np.empty(rows.size, dtype=np.float64)
-    rc = _load().oracle_attention_rows_qk(
+    rc = _load().oracle_attention_rows_dt(
         q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, Nq, Nk, d, float(scale), int(bool(causal)),
-        rows.ctypes.data, rows.size, out.ctypes.data, lse.ctypes.data)
+        rows.ctypes.data, rows.size, out.ctypes.data, lse.ctypes.data, DTYPES[dtype])
     if rc != 0:
-        raise RuntimeError("oracle_attention_rows_qk failed with code %d" % rc)
+        raise RuntimeError("oracle_attention_rows_dt failed with code %d" % rc)
     return out, lse
 
 

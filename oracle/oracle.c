@@ -28,8 +28,8 @@
  * The score row of each query is materialised in full before the softmax, as in
  * the naive three-step attention that "FlashAttention and kernels" contrasts with
  * FlashAttention (section "What naive attention actually does").  Sums run over ascending indices.
- * Inputs are bfloat16 bit patterns; widening bfloat16 to fp64 is exact.
- * Built without -ffast-math.
+ * Inputs are 16-bit patterns of bfloat16 or of IEEE binary16 (fp16); widening
+ * either to fp64 is exact.  Built without -ffast-math.
  */
 #include <math.h>
 #include <stdint.h>
@@ -47,6 +47,29 @@ static double oracle_bf16_to_f64(uint16_t bits) {
   return (double)f;
 }
 
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * Exponent 0 holds zero and the subnormals f * 2^-24; exponent 31 holds the
+ * infinities (f = 0) and NaNs; otherwise (1024 + f) * 2^(e - 25). */
+static double oracle_f16_to_f64(uint16_t bits) {
+  const int sign = bits >> 15, e = (bits >> 10) & 31, f = bits & 1023;
+  double x;
+  if (e == 0)
+    x = ldexp((double)f, -24);
+  else if (e == 31)
+    x = f ? NAN : INFINITY;
+  else
+    x = ldexp((double)(1024 + f), e - 25);
+  return sign ? -x : x;
+}
+
+/* dtype 0: bfloat16, 1: fp16. */
+static double oracle_to_f64(uint16_t bits, int dtype) {
+  return dtype ? oracle_f16_to_f64(bits) : oracle_bf16_to_f64(bits);
+}
+
+/* The element decoder on its own, so that tests can pin it. */
+double oracle_element_to_f64(uint16_t bits, int dtype) { return oracle_to_f64(bits, dtype); }
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();
@@ -63,13 +86,15 @@ int oracle_num_threads(void) {
  * Round 4, causal tile-skipping) compares against; every row keeps key 0).
  * rows: flat query row ids r = (b * H + h) * Nq + i, any order, each in
  * [0, B*H*Nq).  out: nrows * d doubles (row-major), lse: nrows doubles.
+ * dtype: 0 = bfloat16 inputs, 1 = fp16 inputs.
  * Returns 0 on success, 1 on a bad argument, 2 if scratch memory is exhausted.
  */
-int oracle_attention_rows_qk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+int oracle_attention_rows_dt(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, double scale,
                              int causal, const int64_t *rows, int64_t nrows,
-                             double *out, double *lse) {
+                             double *out, double *lse, int dtype) {
   if (!q || !k || !v || !rows || !out || !lse) return 1;
+  if (dtype != 0 && dtype != 1) return 1;
   if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || nrows < 0) return 1;
   const int64_t total_rows = B * H * Nq;
   for (int64_t t = 0; t < nrows; ++t)
@@ -94,12 +119,12 @@ int oracle_attention_rows_qk(const uint16_t *q, const uint16_t *k, const uint16_
         /* keys 0 .. nkeys-1 */
         const int64_t nkeys = (causal && i + 1 < Nk) ? i + 1 : Nk;
 
-        for (int64_t c = 0; c < d; ++c) qi[c] = oracle_bf16_to_f64(q[r * d + c]);
+        for (int64_t c = 0; c < d; ++c) qi[c] = oracle_to_f64(q[r * d + c], dtype);
 
         /* 1. scores of the permitted keys */
         for (int64_t j = 0; j < nkeys; ++j) {
           double acc = 0.0;
-          for (int64_t c = 0; c < d; ++c) acc += qi[c] * oracle_bf16_to_f64(kh[j * d + c]);
+          for (int64_t c = 0; c < d; ++c) acc += qi[c] * oracle_to_f64(kh[j * d + c], dtype);
           s[j] = scale * acc;
         }
         /* 2. row maximum */
@@ -114,7 +139,7 @@ int oracle_attention_rows_qk(const uint16_t *q, const uint16_t *k, const uint16_
         for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
         for (int64_t j = 0; j < nkeys; ++j) {
           const double p = exp(s[j] - m) / l;
-          for (int64_t c = 0; c < d; ++c) o[c] += p * oracle_bf16_to_f64(vh[j * d + c]);
+          for (int64_t c = 0; c < d; ++c) o[c] += p * oracle_to_f64(vh[j * d + c], dtype);
         }
         /* 6. log-sum-exp of the scaled scores, natural log */
         lse[t] = m + log(l);
@@ -124,6 +149,14 @@ int oracle_attention_rows_qk(const uint16_t *q, const uint16_t *k, const uint16_
     free(qi);
   }
   return failed ? 2 : 0;
+}
+
+/* bfloat16 inputs. */
+int oracle_attention_rows_qk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, double scale,
+                             int causal, const int64_t *rows, int64_t nrows,
+                             double *out, double *lse) {
+  return oracle_attention_rows_dt(q, k, v, B, H, Nq, Nk, d, scale, causal, rows, nrows, out, lse, 0);
 }
 
 /* The square case, N queries over N keys: rows r = (b * H + h) * N + i. */
