@@ -74,6 +74,10 @@ def parse():
     ap.add_argument("--flush-reps", type=int, default=10,
                     help="launches per mode timed again with caches flushed before each (0: skip)")
     ap.add_argument("--no-gemm", action="store_true", help="skip the attainable-GEMM reference")
+    ap.add_argument("--dtype", choices=["bf16", "f16"], default="bf16",
+                    help="element type of q, k, v, out (f16 runs through fa_fwd_ex)")
+    ap.add_argument("--headdim", type=int, default=None, choices=[32, 64, 128, 256],
+                    help="override the workload's head dimension (same B, H, N and distributions)")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward (fa_bwd: dQ, dK, dV from the forward's out and LSE) instead")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
@@ -117,7 +121,10 @@ def main():
     fa.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = inputs.WORKLOADS[args.workload]
+    w = dict(inputs.WORKLOADS[args.workload])
+    if args.headdim:
+        w["d"] = args.headdim
+        w["name"] = re.sub(r"-d\d+", "-d%d" % args.headdim, w["name"])
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
     modes = list(w["modes"]) if args.workload != 3 else [0, 1]
     if args.only:
@@ -129,7 +136,7 @@ def main():
     cfg = tuple(int(x) for x in args.cfg.split(",")) if args.cfg else None
 
     t0 = time.time()
-    q_bits, k_bits, v_bits = inputs.make_qkv(args.workload)
+    q_bits, k_bits, v_bits = inputs.make_qkv(args.workload, d=d, dtype=args.dtype)
     print("[bench] inputs %s generated in %.1fs" % (w["name"], time.time() - t0), file=sys.stderr, flush=True)
     Nk = N
     if args.nq is not None:
@@ -138,13 +145,14 @@ def main():
             sys.exit(2)
         q_bits = np.ascontiguousarray(q_bits[:, :, :args.nq])
         N = args.nq
-    general = args.layout == "bnhd" or N != Nk or args.splitkv is not None
-    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    general = args.layout == "bnhd" or N != Nk or args.splitkv is not None or args.dtype != "bf16"
+    tdt = torch.float16 if args.dtype == "f16" else torch.bfloat16
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(tdt).to(dev)
     q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
     if args.layout == "bnhd":
         # stored [B, N, H, d]; the kernel sees [B, H, N, d] views with row stride H*d
         q, k, v = (t.permute(0, 2, 1, 3).contiguous().transpose(1, 2) for t in (q, k, v))
-        outs = {c: torch.empty((B, N, H, d), dtype=torch.bfloat16, device=dev).transpose(1, 2) for c in modes}
+        outs = {c: torch.empty((B, N, H, d), dtype=tdt, device=dev).transpose(1, 2) for c in modes}
     else:
         outs = {c: torch.empty_like(q) for c in modes}
     lses = {c: torch.empty((B, H, N), dtype=torch.float32, device=dev) for c in modes}
@@ -223,6 +231,7 @@ def main():
     roofline = dict(bound="mfma", achieved=dom["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=dom["frac_of_peak"],
                     traffic=measured_traffic(B, H, N, d, dom_c) if not general else None,
+                    peak_note="bf16 and fp16 dense MFMA share the 2.5 PFLOP/s peak",
                     kernel="fa_fwd_kernel d=%d causal=%d cfg=%s" % (d, dom_c, dom["cfg"]),
                     flops_per_launch=flops(B, H, N, d, dom_c, Nk))
     if not args.no_gemm:
@@ -232,16 +241,18 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args, w, modes, q_bits, k_bits, v_bits, scale, outs, lses)
+        cpu = cpu_baseline(args, w, modes, q_bits, k_bits, v_bits, scale, outs, lses, args.dtype)
 
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": (round(value / PAGES_STEP_TFLOPS, 3)
-                        if args.workload == 3 and len(modes) == 2 and N == Nk else None),
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "%s %s%s%s%s" % (w["name"], "+".join("causal" if c else "non-causal" for c in modes),
+                        if args.workload == 3 and len(modes) == 2 and N == Nk and args.dtype == "bf16" and d == 64
+                        else None),
+        "dtype": args.dtype, "data": "synthetic",
+        "config": {"workload": "%s%s %s%s%s%s" % (w["name"], "" if args.dtype == "bf16" else " fp16",
+                                                  "+".join("causal" if c else "non-causal" for c in modes),
                                                 "" if args.layout == "bhnd" else " [B,N,H,d] strided",
                                                 "" if N == Nk else " Nq=%d" % N,
                                                 "" if args.splitkv is None else " split-keys S=%d" % args.splitkv),
@@ -418,11 +429,11 @@ def measured_traffic_bwd(B, H, N, d, causal):
     return int(m.group(1)) if m else None
 
 
-def cpu_baseline(args, w, modes, q_bits, k_bits, v_bits, scale, outs, lses):
+def cpu_baseline(args, w, modes, q_bits, k_bits, v_bits, scale, outs, lses, dtype="bf16"):
     """The oracle, as it stands, on a bounded row sample of the same workload."""
     import torch
     import oracle
-    from inputs import bf16_bits_to_f64, sample_rows, workload_seed
+    from inputs import bits_to_f64, sample_rows, workload_seed
 
     B, H, d = w["B"], w["H"], w["d"]
     N, Nk = q_bits.shape[2], k_bits.shape[2]  # query rows, key rows
@@ -438,11 +449,11 @@ def cpu_baseline(args, w, modes, q_bits, k_bits, v_bits, scale, outs, lses):
     parity = {}
     for c in modes:
         t0 = time.perf_counter()
-        o_ref, l_ref = oracle.attention_rows(q_bits, k_bits, v_bits, scale, bool(c), rows)
+        o_ref, l_ref = oracle.attention_rows(q_bits, k_bits, v_bits, scale, bool(c), rows, dtype=dtype)
         total_s += time.perf_counter() - t0
         nkeys = np.minimum(i + 1, Nk) if c else np.full(rows.shape, Nk)
         total_flops += float(np.sum(4.0 * nkeys * d))
-        o = bf16_bits_to_f64(outs[c].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)).reshape(-1, d)[rows]
+        o = bits_to_f64(outs[c].contiguous().view(torch.int16).cpu().numpy().view(np.uint16), dtype).reshape(-1, d)[rows]
         L = lses[c].cpu().numpy().reshape(-1)[rows]
         err = np.abs(o - o_ref)
         parity["causal" if c else "noncausal"] = dict(

@@ -20,7 +20,7 @@ __all__ = ["fa_fwd", "fa_fwd_ptr", "fa_fwd_cfg", "fa_fwd_ex", "fa_fwd_ex_ptr", "
 
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_cfg", "fa_fwd_ex", "fa_fwd_ex_cfg", "fa_fwd_splitkv",
                     "fa_splitkv_workspace_bytes", "fa_splitkv_default_splits", "fa_default_cfg", "fa_num_variants",
-                    "fa_variant", "fa_strerror", "fa_version", "fa_bwd", "fa_bwd_workspace_bytes")
+                    "fa_variant", "fa_variant_dtype", "fa_strerror", "fa_version", "fa_bwd", "fa_bwd_workspace_bytes")
 
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD_DIM", 4: "FA_ERR_SCALE",
           5: "FA_ERR_ARG", 6: "FA_ERR_ALIGN", 7: "FA_ERR_ALIAS", 8: "FA_ERR_NO_DEVICE",
@@ -52,7 +52,11 @@ class FwdDesc(ctypes.Structure):
                 ("d", ctypes.c_int),
                 ("q_stride", _LL3), ("k_stride", _LL3), ("v_stride", _LL3), ("o_stride", _LL3),
                 ("lse_stride", _LL2),
-                ("scale", ctypes.c_float), ("causal", ctypes.c_int), ("stream", ctypes.c_void_p)]
+                ("scale", ctypes.c_float), ("causal", ctypes.c_int), ("stream", ctypes.c_void_p),
+                ("dtype", ctypes.c_int)]
+
+
+DTYPE_BF16, DTYPE_F16 = 0, 1
 
 
 _lock = threading.Lock()
@@ -91,6 +95,8 @@ def load_library():
             lib.fa_num_variants.restype = _I
             lib.fa_variant.argtypes = [_I, ctypes.POINTER(_I), ctypes.POINTER(_I), ctypes.POINTER(TileCfg)]
             lib.fa_variant.restype = _I
+            lib.fa_variant_dtype.argtypes = [_I]
+            lib.fa_variant_dtype.restype = _I
             lib.fa_strerror.argtypes = [_I]
             lib.fa_strerror.restype = ctypes.c_char_p
             lib.fa_version.argtypes = []
@@ -122,14 +128,17 @@ def default_cfg(N: int, d: int, causal: bool):
     return c.as_tuple()
 
 
-def variants():
-    """Compiled variants as (d, causal, (qb, waves, bk)) tuples."""
+def variants(dtype: str = "bf16"):
+    """Compiled variants of one element type ("bf16" or "f16") as
+    (d, causal, (qb, waves, bk)) tuples."""
     lib = load_library()
+    want = DTYPE_F16 if dtype == "f16" else DTYPE_BF16
     out = []
     for i in range(lib.fa_num_variants()):
         d, c, cfg = _I(), _I(), TileCfg()
         _check(lib.fa_variant(i, ctypes.byref(d), ctypes.byref(c), ctypes.byref(cfg)))
-        out.append((d.value, c.value, cfg.as_tuple()))
+        if lib.fa_variant_dtype(i) == want:
+            out.append((d.value, c.value, cfg.as_tuple()))
     return out
 
 
@@ -207,17 +216,20 @@ def _make_desc(q, k, v, scale, causal, out, lse, stream):
     if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
         raise ValueError("q, k, v must agree on B, H and d")
     Nk = k.shape[2]
+    et = q.dtype
+    if et not in (torch.bfloat16, torch.float16):
+        raise ValueError("q, k, v must be bfloat16 or float16")
     for t in (q, k, v):
-        if t.dtype != torch.bfloat16 or not t.is_cuda or t.stride(3) != 1:
-            raise ValueError("q, k, v must be bfloat16 device views with a contiguous last dimension")
+        if t.dtype != et or not t.is_cuda or t.stride(3) != 1:
+            raise ValueError("q, k, v must be device views of one dtype with a contiguous last dimension")
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
     if out is None:
-        out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((B, H, Nq, d), dtype=et, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if out.shape != (B, H, Nq, d) or out.dtype != torch.bfloat16 or out.stride(3) != 1:
-        raise ValueError("out must be a bf16 [B, H, Nq, d] view with a contiguous last dimension")
+    if out.shape != (B, H, Nq, d) or out.dtype != et or out.stride(3) != 1:
+        raise ValueError("out must be a [B, H, Nq, d] view of q's dtype with a contiguous last dimension")
     if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or lse.stride(2) != 1:
         raise ValueError("lse must be an fp32 [B, H, Nq] view with unit row stride")
     desc = FwdDesc()
@@ -232,18 +244,20 @@ def _make_desc(q, k, v, scale, causal, out, lse, stream):
     desc.scale = float(scale)
     desc.causal = int(bool(causal))
     desc.stream = _stream_handle(stream, q.device)
+    desc.dtype = DTYPE_F16 if et == torch.float16 else DTYPE_BF16
     return desc, out, lse
 
 
 def fa_fwd_ex(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse=None,
               stream=None, cfg=None):
-    """Attention forward on strided torch bf16 views, N_q queries over N_k keys.
+    """Attention forward on strided torch bf16 or fp16 views, N_q queries over N_k keys.
 
     ``q`` is [B, H, Nq, d] and ``k``, ``v`` are [B, H, Nk, d], each with any
     strides whose last one is 1 (a [B, N, H, d] tensor is passed as
     ``t.transpose(1, 2)``).  Causal masking is top-left: key j is visible to
     query i iff j <= i.  ``out`` (default: a new contiguous tensor) is a
-    [B, H, Nq, d] bf16 view, ``lse`` a [B, H, Nq] fp32 view with unit row stride.
+    [B, H, Nq, d] view of q's dtype, ``lse`` a [B, H, Nq] fp32 view with unit
+    row stride.  d is 32, 64, 128 or 256.
     Returns ``(out, lse)``; enqueued on ``stream`` (default: the current stream).
     """
     desc, out, lse = _make_desc(q, k, v, scale, causal, out, lse, stream)

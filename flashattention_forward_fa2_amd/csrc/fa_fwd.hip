@@ -15,56 +15,91 @@
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0
+constexpr int kVersion = 300;  // 0.3.0
 
 using Launcher = hipError_t (*)(const fa::Params&, int B, hipStream_t);
 
 struct Variant {
-  int d, causal, qb, waves, bk;
+  int d, causal, qb, waves, bk, dtype;
   Launcher launch;          // contiguous [B, H, N, d] tensors
   Launcher launch_strided;  // any strides
   Launcher launch_split;    // any strides, one key split per workgroup (p.nsplit splits)
 };
 
-template <int D, bool CAUSAL, int QB, int WAVES, int BK, bool STRIDED, bool SPLIT>
+template <int D, bool CAUSAL, int QB, int WAVES, int BK, bool STRIDED, bool SPLIT, typename E>
 hipError_t launch_variant(const fa::Params& p, int B, hipStream_t stream) {
   using T = fa::Tile<D, QB, WAVES, BK>;
   fa::Params pr = p;
   pr.nqt = (p.Nq + T::kBQ - 1) / T::kBQ;
   const long long blocks = (long long)B * p.H * pr.nqt * (SPLIT ? p.nsplit : 1);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fa::fa_fwd_kernel<D, CAUSAL, QB, WAVES, BK, STRIDED, SPLIT>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((fa::fa_fwd_kernel<D, CAUSAL, QB, WAVES, BK, STRIDED, SPLIT, E>), dim3((unsigned)blocks),
                      dim3(T::kThreads), 0, stream, pr);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, typename E>
 hipError_t launch_merge(const fa::Params& p, hipStream_t stream) {
   const long long rows = (long long)p.BH * p.Nq;
   const long long blocks = (rows + (256 / (D / 4)) - 1) / (256 / (D / 4));
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fa::fa_merge_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream, p, rows);
+  hipLaunchKernelGGL((fa::fa_merge_kernel<D, E>), dim3((unsigned)blocks), dim3(256), 0, stream, p, rows);
   return hipGetLastError();
 }
 
-#define FA_VARIANT(D, C, QB, W, BK)                                                                      \
-  {D, C, QB, W, BK, &launch_variant<D, (C) != 0, QB, W, BK, false, false>,                               \
-   &launch_variant<D, (C) != 0, QB, W, BK, true, false>, &launch_variant<D, (C) != 0, QB, W, BK, true, true>}
+hipError_t run_merge(const fa::Params& p, int d, int dtype, hipStream_t s) {
+  if (dtype == FA_DTYPE_F16) {
+    switch (d) {
+      case 32: return launch_merge<32, fa::F16>(p, s);
+      case 64: return launch_merge<64, fa::F16>(p, s);
+      case 128: return launch_merge<128, fa::F16>(p, s);
+      default: return launch_merge<256, fa::F16>(p, s);
+    }
+  }
+  switch (d) {
+    case 32: return launch_merge<32, fa::Bf16>(p, s);
+    case 64: return launch_merge<64, fa::Bf16>(p, s);
+    case 128: return launch_merge<128, fa::Bf16>(p, s);
+    default: return launch_merge<256, fa::Bf16>(p, s);
+  }
+}
+
+#define FA_VARIANT_T(D, C, QB, W, BK, T, DT)                                                          \
+  {D, C, QB, W, BK, DT, &launch_variant<D, (C) != 0, QB, W, BK, false, false, T>,                     \
+   &launch_variant<D, (C) != 0, QB, W, BK, true, false, T>, &launch_variant<D, (C) != 0, QB, W, BK, true, true, T>}
+#define FA_VARIANT(D, C, QB, W, BK) FA_VARIANT_T(D, C, QB, W, BK, fa::Bf16, FA_DTYPE_BF16)
+#define FA_VARIANT16(D, C, QB, W, BK) FA_VARIANT_T(D, C, QB, W, BK, fa::F16, FA_DTYPE_F16)
 #define FA_VARIANTS_DC(D, C) \
   FA_VARIANT(D, C, 1, 4, 64), FA_VARIANT(D, C, 2, 4, 64), FA_VARIANT(D, C, 1, 8, 64)
+// Head dims 32 and 256 and the fp16 element type: the default tile and the
+// 4-wave tile of the split path (d = 256: 32-key tiles, one configuration).
+#define FA_VARIANTS_SMALL(MAC, D, C) MAC(D, C, 1, 8, 64), MAC(D, C, 1, 4, 64)
 
 const Variant kVariants[] = {
     FA_VARIANTS_DC(64, 0), FA_VARIANTS_DC(64, 1), FA_VARIANTS_DC(128, 0), FA_VARIANTS_DC(128, 1),
+    FA_VARIANTS_SMALL(FA_VARIANT, 32, 0), FA_VARIANTS_SMALL(FA_VARIANT, 32, 1),
+    FA_VARIANT(256, 0, 1, 4, 32), FA_VARIANT(256, 1, 1, 4, 32),
+    FA_VARIANTS_SMALL(FA_VARIANT16, 32, 0), FA_VARIANTS_SMALL(FA_VARIANT16, 32, 1),
+    FA_VARIANTS_SMALL(FA_VARIANT16, 64, 0), FA_VARIANTS_SMALL(FA_VARIANT16, 64, 1),
+    FA_VARIANTS_SMALL(FA_VARIANT16, 128, 0), FA_VARIANTS_SMALL(FA_VARIANT16, 128, 1),
+    FA_VARIANT16(256, 0, 1, 4, 32), FA_VARIANT16(256, 1, 1, 4, 32),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-const Variant* find_variant(int d, int causal, const fa_tile_cfg& c) {
+const Variant* find_variant(int d, int causal, const fa_tile_cfg& c, int dtype = FA_DTYPE_BF16) {
   for (const Variant& v : kVariants)
-    if (v.d == d && v.causal == causal && v.qb == c.qb && v.waves == c.waves && v.bk == c.bk) return &v;
+    if (v.d == d && v.causal == causal && v.dtype == dtype && v.qb == c.qb && v.waves == c.waves && v.bk == c.bk)
+      return &v;
   return nullptr;
 }
 
-fa_tile_cfg default_cfg(int /*N*/, int /*d*/, int /*causal*/) { return fa_tile_cfg{1, 8, 64}; }
+bool head_dim_ok(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+
+// 8 wavefronts of 32 queries, 64-key tiles; d = 256 (512-byte rows, twice the
+// registers per query) takes 4 wavefronts and 32-key tiles.
+fa_tile_cfg default_cfg(int /*N*/, int d, int /*causal*/) {
+  return d == 256 ? fa_tile_cfg{1, 4, 32} : fa_tile_cfg{1, 8, 64};
+}
 
 bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
@@ -76,7 +111,7 @@ int validate(const void* q, const void* k, const void* v, const void* out, const
              int N, int d, float scale, int causal) {
   if (!q || !k || !v || !out || !lse) return FA_ERR_NULL;
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (!head_dim_ok(d)) return FA_ERR_HEAD_DIM;
   const long long elems = (long long)B * H * N * d;
   if ((long long)(N + 256) * d >= (1LL << 30) || elems >= (1LL << 31)) return FA_ERR_SHAPE;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
@@ -121,7 +156,7 @@ bool strides_ok(const long long st[3], int N, int d) {
 int validate_desc(const fa_fwd_desc& a) {
   if (!a.q || !a.k || !a.v || !a.out || !a.lse) return FA_ERR_NULL;
   if (a.B < 1 || a.H < 1 || a.Nq < 1 || a.Nk < 1) return FA_ERR_SHAPE;
-  if (a.d != 64 && a.d != 128) return FA_ERR_HEAD_DIM;
+  if (!head_dim_ok(a.d)) return FA_ERR_HEAD_DIM;
   if ((long long)a.B * a.H > 0x7fffffffLL) return FA_ERR_SHAPE;
   if (!strides_ok(a.q_stride, a.Nq, a.d) || !strides_ok(a.k_stride, a.Nk, a.d) ||
       !strides_ok(a.v_stride, a.Nk, a.d) || !strides_ok(a.o_stride, a.Nq, a.d))
@@ -130,6 +165,7 @@ int validate_desc(const fa_fwd_desc& a) {
     return FA_ERR_STRIDE;
   if (!std::isfinite(a.scale) || !(a.scale > 0.f)) return FA_ERR_SCALE;
   if (a.causal != 0 && a.causal != 1) return FA_ERR_ARG;
+  if (a.dtype != FA_DTYPE_BF16 && a.dtype != FA_DTYPE_F16) return FA_ERR_ARG;
   auto al = [](const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; };
   if (!al(a.q, 16) || !al(a.k, 16) || !al(a.v, 16) || !al(a.out, 16) || !al(a.lse, 4)) return FA_ERR_ALIGN;
   const long long qb = extent_bytes(a.q_stride, a.B, a.H, a.Nq, a.d, 2);
@@ -170,7 +206,7 @@ fa::Params make_params(const fa_fwd_desc& a) {
 int run_desc(const fa_fwd_desc& a, const fa_tile_cfg& cfg) {
   const int st = validate_desc(a);
   if (st != FA_OK) return st;
-  const Variant* var = find_variant(a.d, a.causal, cfg);
+  const Variant* var = find_variant(a.d, a.causal, cfg, a.dtype);
   if (!var) return FA_ERR_ARG;
   const int dst = check_device();
   if (dst != FA_OK) return dst;
@@ -201,9 +237,10 @@ long long split_workspace(int B, int H, int Nq, int d, int S_eff) {
 }
 
 // Tile configuration of the split path: short query ranges (decoding, short
-// prompts) take the 4-wave, 128-query tile, so fewer MFMA rows are padding.
+// prompts) take the 4-wave, 128-query tile, so fewer MFMA rows are padding
+// (d = 256 has 4-wave tiles only).
 fa_tile_cfg split_cfg(int Nq, int Nk, int d, int causal) {
-  return Nq <= 128 ? fa_tile_cfg{1, 4, 64} : default_cfg(Nk, d, causal);
+  return Nq <= 128 && d != 256 ? fa_tile_cfg{1, 4, 64} : default_cfg(Nk, d, causal);
 }
 
 // (the same for both masks, so the workspace query needs no causal flag)
@@ -231,7 +268,7 @@ int run_splitkv(const fa_fwd_desc& a, int num_splits, void* ws, long long ws_byt
       {a.lse, 4 * ((long long)(a.B - 1) * a.lse_stride[0] + (long long)(a.H - 1) * a.lse_stride[1] + a.Nq)}};
   for (const auto& o : others)
     if (overlaps(ws, (size_t)need, o.first, (size_t)o.second)) return FA_ERR_ALIAS;
-  const Variant* var = find_variant(a.d, a.causal, split_cfg(a.Nq, a.Nk, a.d, a.causal));
+  const Variant* var = find_variant(a.d, a.causal, split_cfg(a.Nq, a.Nk, a.d, a.causal), a.dtype);
   if (!var) return FA_ERR_INTERNAL;
   const int dst = check_device();
   if (dst != FA_OK) return dst;
@@ -242,7 +279,7 @@ int run_splitkv(const fa_fwd_desc& a, int num_splits, void* ws, long long ws_byt
   p.part_lse = p.part_o + (long long)S_eff * a.B * a.H * a.Nq * a.d;
   const hipStream_t stream = static_cast<hipStream_t>(a.stream);
   hipError_t e = var->launch_split(p, a.B, stream);
-  if (e == hipSuccess) e = a.d == 64 ? launch_merge<64>(p, stream) : launch_merge<128>(p, stream);
+  if (e == hipSuccess) e = run_merge(p, a.d, a.dtype, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -310,14 +347,14 @@ int fa_fwd_ex_cfg(const fa_fwd_desc* desc, const fa_tile_cfg* cfg) {
 
 int fa_splitkv_default_splits(int B, int H, int Nq, int Nk, int d, int causal) {
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return -FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return -FA_ERR_HEAD_DIM;
+  if (!head_dim_ok(d)) return -FA_ERR_HEAD_DIM;
   (void)causal;
   return default_splits(B, H, Nq, Nk, d);
 }
 
 long long fa_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return -FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return -FA_ERR_HEAD_DIM;
+  if (!head_dim_ok(d)) return -FA_ERR_HEAD_DIM;
   if (num_splits < 0 || num_splits > 1024) return -FA_ERR_ARG;
   const int S = num_splits ? num_splits : default_splits(B, H, Nq, Nk, d);
   return split_workspace(B, H, Nq, d, split_count(Nk, S));
@@ -335,7 +372,7 @@ int fa_fwd_splitkv(const fa_fwd_desc* desc, int num_splits, void* workspace, lon
 int fa_default_cfg(int N, int d, int causal, fa_tile_cfg* cfg) {
   if (!cfg) return FA_ERR_NULL;
   if (N < 1) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (!head_dim_ok(d)) return FA_ERR_HEAD_DIM;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   *cfg = default_cfg(N, d, causal);
   return FA_OK;
@@ -352,14 +389,19 @@ int fa_variant(int i, int* d, int* causal, fa_tile_cfg* cfg) {
   return FA_OK;
 }
 
+int fa_variant_dtype(int i) {
+  if (i < 0 || i >= kNumVariants) return -FA_ERR_ARG;
+  return kVariants[i].dtype;
+}
+
 const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "null pointer argument";
     case FA_ERR_SHAPE: return "B, H, N must be >= 1, tensors below 2^31 elements and (N + 256) * d below 2^30";
-    case FA_ERR_HEAD_DIM: return "head dimension must be 64 or 128";
+    case FA_ERR_HEAD_DIM: return "head dimension must be 32, 64, 128 or 256";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
-    case FA_ERR_ARG: return "invalid argument (causal must be 0 or 1; tile configuration not compiled in)";
+    case FA_ERR_ARG: return "invalid argument (causal must be 0 or 1, dtype bf16 or f16; tile configuration not compiled in)";
     case FA_ERR_ALIGN: return "q, k, v, out must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_ALIAS: return "out/lse overlap an input or each other";
     case FA_ERR_NO_DEVICE: return "no current HIP device, or it is not gfx950";

@@ -15,7 +15,8 @@
 //
 // Scores stay in registers; the N x N matrix never reaches HBM.
 //
-// gfx950 mapping (v_mfma_f32_32x32x16_bf16, accumulators in VGPRs):
+// gfx950 mapping (v_mfma_f32_32x32x16_bf16, or _f16 for fp16 inputs: the element
+// type E only picks the MFMA and the packing; accumulators in VGPRs):
 // * S^T = K Q^T: the A operand is a 16-byte K row segment read from LDS
 //   (ds_read_b128), the B operand a Q row segment held in VGPRs for the whole
 //   sweep.  The 32x32 fp32 result gives each lane ONE query (lane % 32) and 16
@@ -49,6 +50,8 @@ namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -61,6 +64,27 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b);
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b);
+
+// Element types of Q, K, V and O (16 bits each; scores, statistics and
+// accumulators are fp32 either way): the MFMA operand vector, the 32x32x16
+// MFMA, and the round-to-nearest-even packing of two fp32 values.
+struct Bf16 {
+  typedef bf16x8 v8;
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_bf16x2(a, b); }
+};
+struct F16 {
+  typedef f16x8 v8;
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_f16x2(a, b); }
+};
+
 template <int D, int QB, int WAVES, int BK>
 struct Tile {
   static constexpr int kThreads = WAVES * 64;
@@ -71,21 +95,25 @@ struct Tile {
   static constexpr int kLdsBytes = 2 * kStageBytes;       // double-buffered ring
   static constexpr int kBlocks = kTileBytes / 1024;       // 1 KB direct-load blocks per tile
   static constexpr int kBlocksPerWave = (kBlocks + WAVES - 1) / WAVES;
-  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(D == 32 || D == 64 || D == 128 || D == 256, "head dim");
   static_assert(BK % 32 == 0 && BK >= 32 && BK <= 128, "key tile");
   static_assert(kTileBytes % 1024 == 0, "tile = whole 1 KB blocks");
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one CU");
 };
 
 // Swizzle of the 16-byte chunks of LDS row `row` (K and V tiles alike):
-// chunk c is stored at position c ^ swz(row).  For 128-byte rows (d = 64) the
-// position depends on row bits 1..3 (bit-reversed), for 256-byte rows (d = 128)
-// on row bits 0..3 (2-bit fields swapped); both keep the K fragment reads (16
-// rows, one chunk) and the V transpose reads (4 rows, 4 chunks) on distinct
-// banks.
+// chunk c is stored at position c ^ swz(row).  The 64 banks span 256 bytes, so
+// a chunk's bank group is (row * D / 8 + position) mod 16.  For 64-byte rows
+// (d = 32: four rows per bank row) the position depends on row bits 2..3; for
+// 128-byte rows (d = 64) on row bits 1..3 (bit-reversed); for 256- and 512-byte
+// rows (d = 128, 256) on row bits 0..3 (2-bit fields swapped, low four position
+// bits only).  Each keeps the K fragment reads (16 rows, one chunk) and the V
+// transpose reads (4 rows, 4 chunks) on distinct bank groups.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 64) {
+  if constexpr (D == 32) {
+    return (row >> 2) & 3;
+  } else if constexpr (D == 64) {
     const int m = (row >> 1) & 7;
     return ((m & 1) << 2) | (m & 2) | ((m >> 2) & 1);
   } else {
@@ -111,6 +139,12 @@ __device__ __forceinline__ float lane_swap_sum(float x) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   f32x2 f = {a, b};
   bf16x2 h = __builtin_convertvector(f, bf16x2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  f32x2 f = {a, b};
+  f16x2 h = __builtin_convertvector(f, f16x2);
   return __builtin_bit_cast(uint32_t, h);
 }
 
@@ -154,9 +188,10 @@ struct Params {
 // (the per-worker (m, l, o) states that Flash-Decoding merges afterwards:
 // "FlashAttention and kernels", gtadkapally.com, section "FlashAttention-2, -3,
 // and what came after").
-template <int D, bool CAUSAL, int QB, int WAVES, int BK, bool STRIDED, bool SPLIT = false>
+template <int D, bool CAUSAL, int QB, int WAVES, int BK, bool STRIDED, bool SPLIT = false, typename E = Bf16>
 __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
   using T = Tile<D, QB, WAVES, BK>;
+  using v8 = typename E::v8;
   const int BH = pr.BH, Nq = pr.Nq, Nk = pr.Nk, nqt = pr.nqt;
   const float qk_scale = pr.qk_scale;
   const int q_rs = STRIDED ? pr.q_rs : D, k_rs = STRIDED ? pr.k_rs : D;
@@ -212,14 +247,14 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
   const int qw = q0 + wave * (QB * 32);  // first query of this wavefront
 
   // ---- Q block -> VGPRs, as the B operand of S^T = K Q^T (rows >= Nq read 0) ----
-  bf16x8 qreg[QB][D / 16];
+  v8 qreg[QB][D / 16];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qw + qb * 32 + lr;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(qrs, (row * q_rs + ks * 16 + g * 8) * 2, 0, 0);
-      qreg[qb][ks] = __builtin_bit_cast(bf16x8, x);
+      qreg[qb][ks] = __builtin_bit_cast(v8, x);
     }
   }
 
@@ -295,20 +330,19 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
     f32x16 s[QB][BK / 32];
 #pragma unroll
     for (int kb = 0; kb < BK / 32; ++kb) {
-      bf16x8 a[D / 16];
+      v8 a[D / 16];
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
-        a[ks] = *reinterpret_cast<const bf16x8*>(kst + kb * 32 * (D * 2) + koff[ks]);
+        a[ks] = *reinterpret_cast<const v8*>(kst + kb * 32 * (D * 2) + koff[ks]);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], qreg[qb][0], f32x16{}, 0, 0, 0);
+        s[qb][kb] = E::mfma(a[0], qreg[qb][0], f32x16{});
 #pragma unroll
-        for (int ks = 1; ks < D / 16; ++ks)
-          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qreg[qb][ks], s[qb][kb], 0, 0, 0);
+        for (int ks = 1; ks < D / 16; ++ks) s[qb][kb] = E::mfma(a[ks], qreg[qb][ks], s[qb][kb]);
       }
     }
     // ---- V fragments (issued early; consumed after the softmax) --------------
-    bf16x8 va[D / 32][BK / 16];
+    v8 va[D / 32][BK / 16];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -318,10 +352,10 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vst + rowoff + voff[db][1]));
         const u32x4 w = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
                          __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
-        va[db][kk] = __builtin_bit_cast(bf16x8, w);
+        va[db][kk] = __builtin_bit_cast(v8, w);
       }
     // ---- mask, online softmax, P -> bf16 -------------------------------------
-    bf16x8 p[QB][BK / 16];
+    v8 p[QB][BK / 16];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       if (masked) {
@@ -366,8 +400,8 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
         for (int h = 0; h < 2; ++h) {
           u32x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[qb][kb][8 * h + 2 * e], s[qb][kb][8 * h + 2 * e + 1]);
-          p[qb][2 * kb + h] = __builtin_bit_cast(bf16x8, w);
+          for (int e = 0; e < 4; ++e) w[e] = E::pack(s[qb][kb][8 * h + 2 * e], s[qb][kb][8 * h + 2 * e + 1]);
+          p[qb][2 * kb + h] = __builtin_bit_cast(v8, w);
         }
     }
     // ---- O^T += V_j^T P^T ------------------------------------------------------
@@ -377,7 +411,7 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
       for (int kk = 0; kk < BK / 16; ++kk)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][kk], p[qb][kk], oacc[qb][db], 0, 0, 0);
+          oacc[qb][db] = E::mfma(va[db][kk], p[qb][kk], oacc[qb][db]);
   };
 
   auto step = [&](int j, int stage) {
@@ -445,8 +479,8 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           u32x2 w;
-          w[0] = pack_bf16x2(oacc[qb][db][4 * rr + 0] * inv, oacc[qb][db][4 * rr + 1] * inv);
-          w[1] = pack_bf16x2(oacc[qb][db][4 * rr + 2] * inv, oacc[qb][db][4 * rr + 3] * inv);
+          w[0] = E::pack(oacc[qb][db][4 * rr + 0] * inv, oacc[qb][db][4 * rr + 1] * inv);
+          w[1] = E::pack(oacc[qb][db][4 * rr + 2] * inv, oacc[qb][db][4 * rr + 3] * inv);
           *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * rr + 4 * g) = w;
         }
       const long long l_off = STRIDED ? batch * pr.l_sb + hd * pr.l_sh : (long long)bh * Nq;
@@ -462,7 +496,7 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
 // Flash-Decoding paragraph of "FlashAttention-2, -3, and what came after"),
 // applied to states already divided by their own l.  One thread per four
 // consecutive head-dim elements of one row; reads are coalesced along d.
-template <int D>
+template <int D, typename E = Bf16>
 __global__ __launch_bounds__(256) void fa_merge_kernel(const Params pr, long long rows) {
   constexpr int kTPR = D / 4;  // threads per row
   const long long r = (long long)blockIdx.x * (256 / kTPR) + threadIdx.x / kTPR;
@@ -485,8 +519,8 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const Params pr, long lon
   const int batch = bh / pr.H, hd = bh - batch * pr.H;
   uint16_t* orow = pr.out + batch * pr.o_sb + hd * pr.o_sh + (long long)query * pr.o_rs;
   u32x2 w2;
-  w2[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  w2[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  w2[0] = E::pack(acc[0] * inv, acc[1] * inv);
+  w2[1] = E::pack(acc[2] * inv, acc[3] * inv);
   *reinterpret_cast<u32x2*>(orow + c) = w2;
   if (c == 0) pr.lse[batch * pr.l_sb + hd * pr.l_sh + query] = mx + logf(wsum);
 }

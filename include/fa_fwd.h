@@ -32,9 +32,10 @@ enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = 1,       /* a pointer argument is NULL                            */
   FA_ERR_SHAPE = 2,      /* B, H or N < 1, or the sizes overflow the index range  */
-  FA_ERR_HEAD_DIM = 3,   /* d is not 64 or 128                                    */
+  FA_ERR_HEAD_DIM = 3,   /* d is not 32, 64, 128 or 256                           */
   FA_ERR_SCALE = 4,      /* scale is not finite and > 0                           */
-  FA_ERR_ARG = 5,        /* causal not 0/1, or an unknown tile configuration       */
+  FA_ERR_ARG = 5,        /* causal not 0/1, unknown dtype, or a tile configuration
+                            that is not compiled in                               */
   FA_ERR_ALIGN = 6,      /* q, k, v, out not 16-byte aligned, or lse not 4-byte   */
   FA_ERR_ALIAS = 7,      /* out or lse overlaps q, k, v or each other             */
   FA_ERR_NO_DEVICE = 8,  /* no current HIP device, or it is not gfx950            */
@@ -55,7 +56,7 @@ enum fa_status {
  *            log-sum-exp of each query row's scaled scores.  Written.
  *   B, H, N  batch, heads, sequence length (>= 1); B*H*N*d must stay below
  *            2^31 elements per tensor and N*d below 2^31.
- *   d        head dimension: 64 or 128.
+ *   d        head dimension: 32, 64, 128 or 256.
  *   scale    softmax scale applied to q.k (typically 1/sqrt(d)); finite, > 0
  *            (the running maximum is kept in scaled units, which needs scale > 0).
  *   causal   0: every key is visible; 1: key j is visible to query i iff j <= i.
@@ -98,7 +99,8 @@ int fa_fwd_cfg(const void *q, const void *k, const void *v, void *out, float *ls
  * optimise kernels", dev.to, Round 4, causal tile-skipping; N_QUERIES and
  * N_KEYS are separate lengths in "FlashAttention 2 from PyTorch to Triton").
  *
- *   q    bf16, element (b, h, i, c) at q[b*q_stride[0] + h*q_stride[1] + i*q_stride[2] + c],
+ *   q    16-bit elements of type `dtype`, element (b, h, i, c) at
+ *        q[b*q_stride[0] + h*q_stride[1] + i*q_stride[2] + c],
  *        i < Nq;  k, v likewise with i < Nk;  out like q.  The head dimension is
  *        contiguous.  A [B, N, H, d] tensor has strides {N*H*d, d, H*d}.
  *   lse  fp32, element (b, h, i) at lse[b*lse_stride[0] + h*lse_stride[1] + i].
@@ -107,6 +109,10 @@ int fa_fwd_cfg(const void *q, const void *k, const void *v, void *out, float *ls
  * elements (16 bytes), every row stride >= d, and (N + 256) * row stride < 2^30
  * for each tensor's own N, so that one head stays within 32-bit byte offsets.
  * lse strides >= 0.  Pointers: q, k, v, out 16-byte aligned, lse 4-byte.
+ * dtype: FA_DTYPE_BF16 (0, so a zero-initialised descriptor means bfloat16) or
+ * FA_DTYPE_F16 (IEEE binary16) for q, k, v and out alike; scores, the softmax
+ * statistics and the accumulators are fp32 either way and lse is fp32.  fp16
+ * inputs must be finite (|x| <= 65504).
  * Aliasing (FA_ERR_ALIAS) is judged on each tensor's whole byte extent: out
  * and lse must not overlap q, k, v or each other (inputs may overlap each
  * other, e.g. three views of one packed QKV tensor).
@@ -122,7 +128,11 @@ typedef struct fa_fwd_desc {
   float scale;
   int causal;
   void *stream;
+  int dtype;
 } fa_fwd_desc;
+
+/* Element types of fa_fwd_desc.dtype. */
+enum fa_dtype { FA_DTYPE_BF16 = 0, FA_DTYPE_F16 = 1 };
 
 int fa_fwd_ex(const fa_fwd_desc *desc);
 
@@ -164,9 +174,12 @@ int fa_splitkv_default_splits(int B, int H, int Nq, int Nk, int d, int causal);
 /* The configuration fa_fwd picks for (N, d, causal); FA_OK or an error code. */
 int fa_default_cfg(int N, int d, int causal, fa_tile_cfg *cfg);
 
-/* Number of compiled variants, and the i-th one (for d, causal given). */
+/* Number of compiled variants, the i-th one (for d, causal given), and its
+ * element type (an fa_dtype, or minus an error code).  fa_fwd and fa_fwd_cfg
+ * use the bfloat16 variants; fa_fwd_ex and fa_fwd_ex_cfg pick by desc->dtype. */
 int fa_num_variants(void);
 int fa_variant(int i, int *d, int *causal, fa_tile_cfg *cfg);
+int fa_variant_dtype(int i);
 
 /* Static text for a status code. */
 const char *fa_strerror(int status);

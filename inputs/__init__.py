@@ -163,8 +163,10 @@ def default_scale(d: int) -> float:
 
 
 def make_qkv(config: int, B: int | None = None, H: int | None = None, N: int | None = None,
-             d: int | None = None, sigma_qk: float | None = None, sigma_v: float | None = None):
-    """Q, K, V bf16 bit arrays shaped [B, H, N, d] for workload ``config``.
+             d: int | None = None, sigma_qk: float | None = None, sigma_v: float | None = None,
+             dtype: str = "bf16"):
+    """Q, K, V bit arrays (bfloat16, or fp16 with ``dtype="f16"``) shaped
+    [B, H, N, d] for workload ``config``.
 
     Shape and distribution default to the workload's own; overriding them keeps
     the workload's seeds (used by small parity cases).
@@ -177,9 +179,9 @@ def make_qkv(config: int, B: int | None = None, H: int | None = None, N: int | N
     sq = w["sigma_qk"] if sigma_qk is None else sigma_qk
     sv = w["sigma_v"] if sigma_v is None else sigma_v
     count = B * H * N * d
-    q = normal_bf16(workload_seed(config, 0), count, sq).reshape(B, H, N, d)
-    k = normal_bf16(workload_seed(config, 1), count, sq).reshape(B, H, N, d)
-    v = normal_bf16(workload_seed(config, 2), count, sv).reshape(B, H, N, d)
+    q = normal_bits(workload_seed(config, 0), count, sq, dtype).reshape(B, H, N, d)
+    k = normal_bits(workload_seed(config, 1), count, sq, dtype).reshape(B, H, N, d)
+    v = normal_bits(workload_seed(config, 2), count, sv, dtype).reshape(B, H, N, d)
     return q, k, v
 
 

@@ -47,12 +47,13 @@ def test_strerror_and_version(lib):
 
 
 def test_variant_table(lib):
-    vs = fa.variants()
-    assert len(vs) >= 4  # both head dims x both modes
-    for d in (64, 128):
-        for causal in (0, 1):
-            assert any(v[0] == d and v[1] == causal for v in vs)
-            assert (d, causal, fa.default_cfg(4096, d, causal)) in vs
+    for dtype in ("bf16", "f16"):
+        vs = fa.variants(dtype)
+        for d in (32, 64, 128, 256):
+            for causal in (0, 1):
+                assert (d, causal, fa.default_cfg(4096, d, causal)) in vs, (dtype, d, causal)
+    assert lib.fa_variant_dtype(-1) < 0 and lib.fa_variant_dtype(lib.fa_num_variants()) < 0
+    assert len(fa.variants("bf16")) + len(fa.variants("f16")) == lib.fa_num_variants()
 
 
 FAKE = 1 << 20  # 16-byte aligned, never dereferenced: checks fail before any HIP call
@@ -68,7 +69,7 @@ def call(q=FAKE, k=2 * FAKE, v=3 * FAKE, out=4 * FAKE, lse=5 * FAKE, B=1, H=1, N
     (dict(B=0), 2), (dict(H=-1), 2), (dict(N=0), 2),
     (dict(B=1 << 12, H=1 << 12, N=1 << 10), 2),
     (dict(N=1 << 24, d=128), 2),
-    (dict(d=32), 3), (dict(d=96), 3), (dict(d=256), 3),
+    (dict(d=16), 3), (dict(d=96), 3), (dict(d=512), 3),
     (dict(scale=0.0), 4), (dict(scale=-0.1), 4), (dict(scale=float("inf")), 4), (dict(scale=float("nan")), 4),
     (dict(causal=2), 5), (dict(causal=-1), 5),
     (dict(q=FAKE + 8), 6), (dict(out=4 * FAKE + 4), 6), (dict(lse=5 * FAKE + 2), 6),
@@ -111,15 +112,15 @@ def test_desc_layout_matches_the_header(tmp_path):
     src = tmp_path / "sz.c"
     src.write_text(
         "#include <stdio.h>\n#include <stddef.h>\n#include \"fa_fwd.h\"\n"
-        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu\\n\", sizeof(fa_fwd_desc),"
+        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu %zu\\n\", sizeof(fa_fwd_desc),"
         " offsetof(fa_fwd_desc, B), offsetof(fa_fwd_desc, q_stride), offsetof(fa_fwd_desc, lse_stride),"
-        " offsetof(fa_fwd_desc, scale), offsetof(fa_fwd_desc, stream)); return 0;}\n")
+        " offsetof(fa_fwd_desc, scale), offsetof(fa_fwd_desc, stream), offsetof(fa_fwd_desc, dtype)); return 0;}\n")
     exe = tmp_path / "sz"
     assert os.system("gcc -I %s -o %s %s" % (os.path.join(ROOT, "include"), exe, src)) == 0
     got = [int(x) for x in os.popen(str(exe)).read().split()]
     D = fa.FwdDesc
     assert got == [ctypes.sizeof(D), D.B.offset, D.q_stride.offset, D.lse_stride.offset, D.scale.offset,
-                   D.stream.offset]
+                   D.stream.offset, D.dtype.offset]
 
 
 def desc(**kw):
@@ -150,7 +151,8 @@ def desc(**kw):
     (dict(v_stride=(8192, -4096, 64)), 11),           # negative
     (dict(o_stride=(8192, 4096, 1 << 24)), 11),       # a head beyond 32-bit offsets
     (dict(lse_stride=(-1, 64)), 11),
-    (dict(scale=0.0), 4), (dict(causal=3), 5),
+    (dict(scale=0.0), 4), (dict(causal=3), 5), (dict(dtype=2), 5), (dict(dtype=-1), 5),
+    (dict(d=48), 3),
     (dict(k=2 * FAKE + 8), 6), (dict(lse=5 * FAKE + 2), 6),
     (dict(out=3 * FAKE), 7), (dict(lse=FAKE + 256), 7),
 ])
@@ -172,6 +174,9 @@ def test_desc_valid_layouts_reach_the_device_check(lib):
     B, H, N, d = 2, 4, 128, 64
     bnhd = (N * H * d, d, H * d)
     assert fa.fa_fwd_ex_ptr(desc(Nq=17, Nk=300)) == 8
+    for d in (32, 256):                                     # the other head dims, both element types
+        for dt in (0, 1):
+            assert fa.fa_fwd_ex_ptr(desc(d=d, dtype=dt)) == 8
     assert fa.fa_fwd_ex_ptr(desc(B=B, H=H, Nq=N, Nk=N, q_stride=bnhd, k_stride=bnhd, v_stride=bnhd,
                                  o_stride=bnhd, out=8 * FAKE)) == 8
     packed = (N * 3 * H * d, d, 3 * H * d)  # [B, N, 3, H, d]: q, k, v interleaved
