@@ -67,8 +67,19 @@ _I = ctypes.c_int
 
 
 def load_library():
-    """Load libfa_fwd.so from the package directory (raises if it is not built)."""
+    """Load libfa_fwd.so from the package directory (raises if it is not built).
+
+    torch (when installed) is imported first: its wheel ships its own HIP
+    runtime, which this library must share.  Loaded before torch, the library
+    would pull in the system runtime under another file name, torch would then
+    load its own, and with two HIP runtimes in one process the one this library
+    uses reports no device.
+    """
     global _lib
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     with _lock:
         if _lib is None:
             if not os.path.exists(LIB):

@@ -13,6 +13,10 @@
 //   m_new = max(m, rowmax(S)),  alpha = exp(m - m_new),
 //   l     = alpha*l + rowsum(exp(S - m_new)),  O = alpha*O + exp(S - m_new) V.
 //
+// (here with a lazy m: it is raised only when rowmax(S) exceeds it by more than
+// a fixed margin, which leaves O / l and m + log l unchanged and skips most
+// rescales; see kLazyMax).
+//
 // Scores stay in registers; the N x N matrix never reaches HBM.
 //
 // gfx950 mapping (v_mfma_f32_32x32x16_bf16, or _f16 for fp16 inputs: the element
@@ -27,7 +31,10 @@
 //   through ds_read_b64_tr_b16, which hands each lane one head-dim column of a
 //   4-key x 16-column block; the key order inside each 16-key step matches the
 //   order in which the S^T accumulator holds the keys.  The alpha rescale of O
-//   is a per-lane scalar multiply, skipped when no lane's maximum moved.
+//   is a per-lane scalar multiply, skipped when no lane's reference maximum
+//   moved; the reference moves only when a tile's maximum passes it by more
+//   than kLazyMax (a factor 2^8 in P), so after a row's first tiles it rarely
+//   does.
 // * K and V tiles go HBM -> LDS directly (buffer_load_dwordx4 ... lds), 16 bytes
 //   per lane; rows past the last key fall outside the buffer's range and read
 //   as zero.
@@ -62,6 +69,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLazyMax = 8.0f;  // see the online-softmax update in fa_fwd_kernel
 constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b);
@@ -374,7 +382,13 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
 #pragma unroll
         for (int r = (kb == 0 ? 2 : 0); r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
       mx = lane_swap_max(mx);
-      const float m_new = fmaxf(m[qb], mx * qk_scale);
+      // Lazy reference maximum: m moves only when the tile's maximum exceeds it
+      // by more than kLazyMax (log2 units); until then P may reach 2^kLazyMax,
+      // far from fp32 / bf16 / fp16 overflow for P and O.  O / l and
+      // LSE = m + log2 l hold for any reference m, and most tiles then skip
+      // the O rescale.
+      const float mt = mx * qk_scale;
+      const float m_new = (mt > m[qb] + kLazyMax) ? mt : m[qb];
       // A row that has seen no visible key yet keeps m = -inf; subtract 0 then
       // so that exp2(-inf - (-inf)) never appears.
       const float m_sub = (m_new == -__builtin_inff()) ? 0.f : m_new;
