@@ -438,3 +438,44 @@ def test_merge_with_empty_state_is_identity():
     a = osm.update(osm.RowState(), [0.5, -1.0], np.eye(2))
     for m in (osm.merge(a, osm.RowState()), osm.merge(osm.RowState(), a)):
         assert m.m == a.m and m.l == a.l and np.array_equal(m.o, a.o)
+
+
+def _lazy_row(scores, values, block, margin):
+    """The recurrence with a lazy reference maximum (the GPU kernel's variant):
+    the reference m moves to a block's maximum only when that maximum exceeds m
+    by more than `margin`; O / l and m + ln l are then used as usual."""
+    m, l, o = -math.inf, 0.0, np.zeros(values.shape[1])
+    for a in range(0, len(scores), block):
+        s = np.asarray(scores[a:a + block])
+        bm = s.max()
+        m_new = bm if bm > m + margin else m
+        alpha = 0.0 if m == -math.inf else math.exp(m - m_new)
+        p = np.exp(s - m_new)
+        l = alpha * l + p.sum()
+        o = alpha * o + p @ values[a:a + block]
+        m = m_new
+    return o / l, m + math.log(l)
+
+
+@pytest.mark.parametrize("margin", [0.0, 8.0 * math.log(2.0), 30.0])
+def test_lazy_reference_maximum_equals_definition(margin):
+    """O = sum P V / sum P and LSE = m + ln l hold for any reference m, so a
+    maximum that lags the true one by up to the margin gives the definition's
+    result (here against the oracle, with an increasing score sequence that
+    forces the reference to move, and a late maximum)."""
+    rng = np.random.default_rng(9)
+    N, d = 300, 8
+    q, k, v = random_qkv(900, 1, 1, N, d, sigma_qk=2.0)
+    qf, kf, vf = (bf16_bits_to_f64(a)[0, 0] for a in (q, k, v))
+    scale = f32(1 / math.sqrt(d))
+    kf = kf * np.linspace(0.2, 3.0, N)[:, None]          # scores of row 0 drift upward
+    k2 = f64_to_bf16_bits(kf).reshape(1, 1, N, d)
+    kf = bf16_bits_to_f64(k2)[0, 0]
+    rows = np.array([0, 7, N - 1])
+    out, lse = oracle.attention_rows(q, k2, v, scale, False, rows)
+    for t, i in enumerate(rows):
+        s = [scale * float(qf[i] @ kf[j]) for j in range(N)]
+        for block in (16, 64):
+            o, L = _lazy_row(s, vf, block, margin)
+            assert np.allclose(o, out[t], atol=1e-11, rtol=1e-11)
+            assert abs(L - lse[t]) < 1e-11
