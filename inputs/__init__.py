@@ -110,6 +110,8 @@ def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def bits_to_f64(bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    if dtype == "f32":
+        return np.asarray(bits, dtype=np.float32).astype(np.float64)
     return f16_bits_to_f64(bits) if dtype == "f16" else bf16_bits_to_f64(bits)
 
 
@@ -123,7 +125,20 @@ def normal_f16(seed: int, count: int, sigma: float = 1.0) -> np.ndarray:
     return out
 
 
+def normal_f32(seed: int, count: int, sigma: float = 1.0) -> np.ndarray:
+    """``count`` i.i.d. N(0, sigma^2) values rounded to fp32 (the same draws as
+    ``normal_bf16`` for the same seed)."""
+    out = np.empty(count, dtype=np.float32)
+    for s in range(0, count, _CHUNK):
+        n = min(_CHUNK, count - s)
+        out[s:s + n] = (_normals_f64(seed, s, n) * float(sigma)).astype(np.float32)
+    return out
+
+
 def normal_bits(seed: int, count: int, sigma: float = 1.0, dtype: str = "bf16") -> np.ndarray:
+    """bf16 / f16: uint16 bit patterns; f32: float32 values."""
+    if dtype == "f32":
+        return normal_f32(seed, count, sigma)
     return normal_f16(seed, count, sigma) if dtype == "f16" else normal_bf16(seed, count, sigma)
 
 

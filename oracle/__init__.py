@@ -58,6 +58,8 @@ def _load():
                 ctypes.c_void_p, ctypes.c_void_p]
             lib.oracle_attention_rows_dt.restype = ctypes.c_int
             lib.oracle_attention_rows_dt.argtypes = lib.oracle_attention_rows_qk.argtypes + [ctypes.c_int]
+            lib.oracle_attention_rows_f32.restype = ctypes.c_int
+            lib.oracle_attention_rows_f32.argtypes = lib.oracle_attention_rows_qk.argtypes
             lib.oracle_element_to_f64.restype = ctypes.c_double
             lib.oracle_element_to_f64.argtypes = [ctypes.c_uint16, ctypes.c_int]
             lib.oracle_attention_bwd.restype = ctypes.c_int
@@ -110,6 +112,27 @@ def attention_rows(q, k, v, scale: float, causal: bool, rows=None, dtype: str = 
         rows.ctypes.data, rows.size, out.ctypes.data, lse.ctypes.data, DTYPES[dtype])
     if rc != 0:
         raise RuntimeError("oracle_attention_rows_dt failed with code %d" % rc)
+    return out, lse
+
+
+def attention_rows_f32(q, k, v, scale: float, causal: bool, rows=None):
+    """``attention_rows`` for fp32 inputs: ``q`` float32 [B, H, Nq, d], ``k, v``
+    float32 [B, H, Nk, d]."""
+    q, k, v = (np.ascontiguousarray(a, dtype=np.float32) for a in (q, k, v))
+    if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError("q must be [B, H, Nq, d] and k, v one [B, H, Nk, d] shape")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if rows is None:
+        rows = np.arange(B * H * Nq, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, d), dtype=np.float64)
+    lse = np.empty(rows.size, dtype=np.float64)
+    rc = _load().oracle_attention_rows_f32(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, Nq, Nk, d, float(scale), int(bool(causal)),
+        rows.ctypes.data, rows.size, out.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_attention_rows_f32 failed with code %d" % rc)
     return out, lse
 
 

@@ -151,6 +151,57 @@ int oracle_attention_rows_dt(const uint16_t *q, const uint16_t *k, const uint16_
   return failed ? 2 : 0;
 }
 
+/*
+ * The same definition for fp32 inputs (q [B, H, Nq, d], k and v [B, H, Nk, d]
+ * as IEEE binary32 values; widening to fp64 is exact).  Arguments and return
+ * codes as oracle_attention_rows_dt.
+ */
+int oracle_attention_rows_f32(const float *q, const float *k, const float *v,
+                              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, double scale,
+                              int causal, const int64_t *rows, int64_t nrows,
+                              double *out, double *lse) {
+  if (!q || !k || !v || !rows || !out || !lse) return 1;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || nrows < 0) return 1;
+  const int64_t total_rows = B * H * Nq;
+  for (int64_t t = 0; t < nrows; ++t)
+    if (rows[t] < 0 || rows[t] >= total_rows) return 1;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double *s = (double *)malloc((size_t)Nk * sizeof(double));
+    if (!s) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t t = 0; t < nrows; ++t) {
+        const int64_t r = rows[t], head = r / Nq, i = r % Nq;
+        const float *qi = q + r * d, *kh = k + head * Nk * d, *vh = v + head * Nk * d;
+        const int64_t nkeys = (causal && i + 1 < Nk) ? i + 1 : Nk;
+        for (int64_t j = 0; j < nkeys; ++j) {
+          double acc = 0.0;
+          for (int64_t c = 0; c < d; ++c) acc += (double)qi[c] * (double)kh[j * d + c];
+          s[j] = scale * acc;
+        }
+        double m = s[0];
+        for (int64_t j = 1; j < nkeys; ++j)
+          if (s[j] > m) m = s[j];
+        double l = 0.0;
+        for (int64_t j = 0; j < nkeys; ++j) l += exp(s[j] - m);
+        double *o = out + t * d;
+        for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+        for (int64_t j = 0; j < nkeys; ++j) {
+          const double p = exp(s[j] - m) / l;
+          for (int64_t c = 0; c < d; ++c) o[c] += p * (double)vh[j * d + c];
+        }
+        lse[t] = m + log(l);
+      }
+    }
+    free(s);
+  }
+  return failed ? 2 : 0;
+}
+
 /* bfloat16 inputs. */
 int oracle_attention_rows_qk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, double scale,

@@ -80,3 +80,38 @@ def test_same_normals_in_both_dtypes():
     a = f16_bits_to_f64(normal_f16(77, 4096))
     b = bf16_bits_to_f64(normal_bf16(77, 4096))
     assert np.all(np.abs(a - b) <= np.abs(b) * 2.0 ** -8 + 2.0 ** -24)
+
+
+# ---------------------------------------------------------------- fp32 inputs
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal", [(1, 1, 7, 7, 8, False), (1, 2, 9, 9, 64, True),
+                                                (2, 1, 5, 13, 16, True), (1, 1, 12, 30, 128, False)])
+def test_brute_force_f32(B, H, Nq, Nk, d, causal):
+    """fp32 inputs carry 24-bit significands: the oracle reads them at full precision."""
+    q, _, _ = random_qkv(700 + Nq + d, B, H, Nq, d, dtype="f32")
+    _, k, v = random_qkv(710 + Nk + d, B, H, Nk, d, dtype="f32")
+    scale = float(np.float32(1 / math.sqrt(d)))
+    out, lse = oracle.attention_rows_f32(q, k, v, scale, causal)
+    qf = q.astype(np.float64).reshape(B * H, Nq, d)
+    kf, vf = (a.astype(np.float64).reshape(B * H, Nk, d) for a in (k, v))
+    for bh in range(B * H):
+        for i in range(Nq):
+            n = min(i + 1, Nk) if causal else Nk
+            o, L = brute_force_row(qf[bh, i], kf[bh], vf[bh], scale, n)
+            t = bh * Nq + i
+            assert np.allclose(out[t], o, atol=1e-13, rtol=1e-12)
+            assert abs(lse[t] - L) < 1e-12
+
+
+def test_f32_values_are_not_rounded():
+    """Identical keys: each row is the exact mean of the visible value rows, whose
+    values need fp32's full significand (1 + 2^-20 steps), so any rounding to a
+    16-bit format would show."""
+    rng = np.random.default_rng(13)
+    N, d = 6, 8
+    vals = (1.0 + rng.integers(0, 1 << 20, size=(N, d)) * 2.0 ** -20).astype(np.float32)
+    kk = np.tile(rng.standard_normal(d).astype(np.float32), (N, 1)).reshape(1, 1, N, d)
+    qq = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    out, _ = oracle.attention_rows_f32(qq, kk, vals.reshape(1, 1, N, d), 0.5, True)
+    for i in range(N):
+        assert np.allclose(out[i], vals[: i + 1].astype(np.float64).mean(axis=0), atol=1e-15, rtol=1e-15)
