@@ -31,7 +31,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (fp16 the same)
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd TFLOP/s (bf16, causal + non-causal) and % of bf16 MFMA peak"
 # The pages' figures for this exact workload (RTX 4070 SUPER, Triton): 1.954 ms
@@ -74,8 +75,8 @@ def parse():
     ap.add_argument("--flush-reps", type=int, default=10,
                     help="launches per mode timed again with caches flushed before each (0: skip)")
     ap.add_argument("--no-gemm", action="store_true", help="skip the attainable-GEMM reference")
-    ap.add_argument("--dtype", choices=["bf16", "f16"], default="bf16",
-                    help="element type of q, k, v, out (f16 runs through fa_fwd_ex)")
+    ap.add_argument("--dtype", choices=["bf16", "f16", "f32"], default="bf16",
+                    help="element type of q, k, v, out (f16 and f32 run through fa_fwd_ex)")
     ap.add_argument("--headdim", type=int, default=None, choices=[32, 64, 128, 256],
                     help="override the workload's head dimension (same B, H, N and distributions)")
     ap.add_argument("--bwd", action="store_true",
@@ -146,8 +147,12 @@ def main():
         q_bits = np.ascontiguousarray(q_bits[:, :, :args.nq])
         N = args.nq
     general = args.layout == "bnhd" or N != Nk or args.splitkv is not None or args.dtype != "bf16"
-    tdt = torch.float16 if args.dtype == "f16" else torch.bfloat16
-    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(tdt).to(dev)
+    tdt = {"f16": torch.float16, "f32": torch.float32}.get(args.dtype, torch.bfloat16)
+    if args.dtype == "f32":
+        to_dev = lambda a: torch.from_numpy(a).to(dev)
+    else:
+        to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(tdt).to(dev)
+    peak = PEAK_F32_TFLOPS if args.dtype == "f32" else PEAK_BF16_TFLOPS
     q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
     if args.layout == "bnhd":
         # stored [B, N, H, d]; the kernel sees [B, H, N, d] views with row stride H*d
@@ -207,9 +212,9 @@ def main():
             kernel_ms_avg=round(avg, 5), kernel_ms_median=round(float(np.median(ms)), 5),
             kernel_ms_min=round(float(ms.min()), 5), kernel_ms_max=round(float(ms.max()), 5),
             tflops=round(tf, 2),
-            frac_of_peak=round(tf / PEAK_BF16_TFLOPS, 4),
+            frac_of_peak=round(tf / peak, 4),
             hbm_gbs=round((4.0 * B * H * N * d + 4.0 * B * H * Nk * d + 4.0 * B * H * N) / (avg * 1e-3) / 1e9, 1),
-            cfg=list(cfg if cfg else fa.default_cfg(N, d, bool(c))))
+            cfg=list(cfg if cfg else ((1, 4, 32) if args.dtype == "f32" else fa.default_cfg(N, d, bool(c)))))
     # Outside the timed region: each mode again with the caches flushed before
     # every launch (a 512 MiB write, more than L2 and the 256 MB Infinity Cache).
     if args.flush_reps > 0:
@@ -228,10 +233,11 @@ def main():
         del junk
     dom_c = max(modes, key=lambda c: per_mode["causal" if c else "noncausal"]["kernel_ms_avg"])
     dom = per_mode["causal" if dom_c else "noncausal"]
-    roofline = dict(bound="mfma", achieved=dom["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+    roofline = dict(bound="mfma", achieved=dom["tflops"], peak=peak, unit="TFLOP/s",
                     frac=dom["frac_of_peak"],
                     traffic=measured_traffic(B, H, N, d, dom_c) if not general else None,
-                    peak_note="bf16 and fp16 dense MFMA share the 2.5 PFLOP/s peak",
+                    peak_note=("fp32 dense MFMA peak" if args.dtype == "f32"
+                               else "bf16 and fp16 dense MFMA share the 2.5 PFLOP/s peak"),
                     kernel="fa_fwd_kernel d=%d causal=%d cfg=%s" % (d, dom_c, dom["cfg"]),
                     flops_per_launch=flops(B, H, N, d, dom_c, Nk))
     if not args.no_gemm:
@@ -251,7 +257,7 @@ def main():
                         if args.workload == 3 and len(modes) == 2 and N == Nk and args.dtype == "bf16" and d == 64
                         else None),
         "dtype": args.dtype, "data": "synthetic",
-        "config": {"workload": "%s%s %s%s%s%s" % (w["name"], "" if args.dtype == "bf16" else " fp16",
+        "config": {"workload": "%s%s %s%s%s%s" % (w["name"], {"bf16": "", "f16": " fp16", "f32": " fp32"}[args.dtype],
                                                   "+".join("causal" if c else "non-causal" for c in modes),
                                                 "" if args.layout == "bhnd" else " [B,N,H,d] strided",
                                                 "" if N == Nk else " Nq=%d" % N,
@@ -449,11 +455,17 @@ def cpu_baseline(args, w, modes, q_bits, k_bits, v_bits, scale, outs, lses, dtyp
     parity = {}
     for c in modes:
         t0 = time.perf_counter()
-        o_ref, l_ref = oracle.attention_rows(q_bits, k_bits, v_bits, scale, bool(c), rows, dtype=dtype)
+        if dtype == "f32":
+            o_ref, l_ref = oracle.attention_rows_f32(q_bits, k_bits, v_bits, scale, bool(c), rows)
+        else:
+            o_ref, l_ref = oracle.attention_rows(q_bits, k_bits, v_bits, scale, bool(c), rows, dtype=dtype)
         total_s += time.perf_counter() - t0
         nkeys = np.minimum(i + 1, Nk) if c else np.full(rows.shape, Nk)
         total_flops += float(np.sum(4.0 * nkeys * d))
-        o = bits_to_f64(outs[c].contiguous().view(torch.int16).cpu().numpy().view(np.uint16), dtype).reshape(-1, d)[rows]
+        if dtype == "f32":
+            o = outs[c].contiguous().cpu().numpy().astype(np.float64).reshape(-1, d)[rows]
+        else:
+            o = bits_to_f64(outs[c].contiguous().view(torch.int16).cpu().numpy().view(np.uint16), dtype).reshape(-1, d)[rows]
         L = lses[c].cpu().numpy().reshape(-1)[rows]
         err = np.abs(o - o_ref)
         parity["causal" if c else "noncausal"] = dict(

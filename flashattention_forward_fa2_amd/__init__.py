@@ -56,7 +56,8 @@ class FwdDesc(ctypes.Structure):
                 ("dtype", ctypes.c_int)]
 
 
-DTYPE_BF16, DTYPE_F16 = 0, 1
+DTYPE_BF16, DTYPE_F16, DTYPE_F32 = 0, 1, 2
+_DTYPE_NAMES = {"bf16": DTYPE_BF16, "f16": DTYPE_F16, "f32": DTYPE_F32}
 
 
 _lock = threading.Lock()
@@ -140,10 +141,10 @@ def default_cfg(N: int, d: int, causal: bool):
 
 
 def variants(dtype: str = "bf16"):
-    """Compiled variants of one element type ("bf16" or "f16") as
+    """Compiled variants of one element type ("bf16", "f16" or "f32") as
     (d, causal, (qb, waves, bk)) tuples."""
     lib = load_library()
-    want = DTYPE_F16 if dtype == "f16" else DTYPE_BF16
+    want = _DTYPE_NAMES[dtype]
     out = []
     for i in range(lib.fa_num_variants()):
         d, c, cfg = _I(), _I(), TileCfg()
@@ -228,8 +229,8 @@ def _make_desc(q, k, v, scale, causal, out, lse, stream):
         raise ValueError("q, k, v must agree on B, H and d")
     Nk = k.shape[2]
     et = q.dtype
-    if et not in (torch.bfloat16, torch.float16):
-        raise ValueError("q, k, v must be bfloat16 or float16")
+    if et not in (torch.bfloat16, torch.float16, torch.float32):
+        raise ValueError("q, k, v must be bfloat16, float16 or float32")
     for t in (q, k, v):
         if t.dtype != et or not t.is_cuda or t.stride(3) != 1:
             raise ValueError("q, k, v must be device views of one dtype with a contiguous last dimension")
@@ -255,20 +256,20 @@ def _make_desc(q, k, v, scale, causal, out, lse, stream):
     desc.scale = float(scale)
     desc.causal = int(bool(causal))
     desc.stream = _stream_handle(stream, q.device)
-    desc.dtype = DTYPE_F16 if et == torch.float16 else DTYPE_BF16
+    desc.dtype = {torch.float16: DTYPE_F16, torch.float32: DTYPE_F32}.get(et, DTYPE_BF16)
     return desc, out, lse
 
 
 def fa_fwd_ex(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse=None,
               stream=None, cfg=None):
-    """Attention forward on strided torch bf16 or fp16 views, N_q queries over N_k keys.
+    """Attention forward on strided torch bf16, fp16 or fp32 views, N_q queries over N_k keys.
 
     ``q`` is [B, H, Nq, d] and ``k``, ``v`` are [B, H, Nk, d], each with any
     strides whose last one is 1 (a [B, N, H, d] tensor is passed as
     ``t.transpose(1, 2)``).  Causal masking is top-left: key j is visible to
     query i iff j <= i.  ``out`` (default: a new contiguous tensor) is a
     [B, H, Nq, d] view of q's dtype, ``lse`` a [B, H, Nq] fp32 view with unit
-    row stride.  d is 32, 64, 128 or 256.
+    row stride.  d is 32, 64, 128 or 256 (fp32: 64 or 128).
     Returns ``(out, lse)``; enqueued on ``stream`` (default: the current stream).
     """
     desc, out, lse = _make_desc(q, k, v, scale, causal, out, lse, stream)

@@ -20,7 +20,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
-def source_digest(names=("fa_fwd_kernel.hpp", "fa_fwd.hip")) -> str:
+def source_digest(names=("fa_fwd_kernel.hpp", "fa_fwd_f32_kernel.hpp", "fa_fwd.hip")) -> str:
     """sha256 over kernel sources and the device flags: identifies the compiled
     kernels, so that measurements taken on one build are not reported for
     another.  The default covers the forward; pass ``BWD_SOURCES`` for the

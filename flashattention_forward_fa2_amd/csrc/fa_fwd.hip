@@ -11,11 +11,12 @@
 #include <mutex>
 #include <utility>
 
+#include "fa_fwd_f32_kernel.hpp"
 #include "fa_fwd_kernel.hpp"
 
 namespace {
 
-constexpr int kVersion = 300;  // 0.3.0
+constexpr int kVersion = 310;  // 0.3.1
 
 using Launcher = hipError_t (*)(const fa::Params&, int B, hipStream_t);
 
@@ -47,6 +48,18 @@ hipError_t launch_merge(const fa::Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// fp32 inputs: 4 wavefronts of 32 queries, BK-key tiles (no split variant).
+template <int D, bool CAUSAL, int WAVES, int BK, bool STRIDED>
+hipError_t launch_f32(const fa::Params& p, int B, hipStream_t stream) {
+  fa::Params pr = p;
+  pr.nqt = (p.Nq + WAVES * 32 - 1) / (WAVES * 32);
+  const long long blocks = (long long)B * p.H * pr.nqt;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fa::fa_fwd_f32_kernel<D, CAUSAL, WAVES, BK, STRIDED>), dim3((unsigned)blocks),
+                     dim3(WAVES * 64), 0, stream, pr);
+  return hipGetLastError();
+}
+
 hipError_t run_merge(const fa::Params& p, int d, int dtype, hipStream_t s) {
   if (dtype == FA_DTYPE_F16) {
     switch (d) {
@@ -69,6 +82,9 @@ hipError_t run_merge(const fa::Params& p, int d, int dtype, hipStream_t s) {
    &launch_variant<D, (C) != 0, QB, W, BK, true, false, T>, &launch_variant<D, (C) != 0, QB, W, BK, true, true, T>}
 #define FA_VARIANT(D, C, QB, W, BK) FA_VARIANT_T(D, C, QB, W, BK, fa::Bf16, FA_DTYPE_BF16)
 #define FA_VARIANT16(D, C, QB, W, BK) FA_VARIANT_T(D, C, QB, W, BK, fa::F16, FA_DTYPE_F16)
+#define FA_VARIANT32(D, C, W, BK)                                                                        \
+  {D, C, 1, W, BK, FA_DTYPE_F32, &launch_f32<D, (C) != 0, W, BK, false>, &launch_f32<D, (C) != 0, W, BK, true>, \
+   nullptr}
 #define FA_VARIANTS_DC(D, C) \
   FA_VARIANT(D, C, 1, 4, 64), FA_VARIANT(D, C, 2, 4, 64), FA_VARIANT(D, C, 1, 8, 64)
 // Head dims 32 and 256 and the fp16 element type: the default tile and the
@@ -83,6 +99,8 @@ const Variant kVariants[] = {
     FA_VARIANTS_SMALL(FA_VARIANT16, 64, 0), FA_VARIANTS_SMALL(FA_VARIANT16, 64, 1),
     FA_VARIANTS_SMALL(FA_VARIANT16, 128, 0), FA_VARIANTS_SMALL(FA_VARIANT16, 128, 1),
     FA_VARIANT16(256, 0, 1, 4, 32), FA_VARIANT16(256, 1, 1, 4, 32),
+    FA_VARIANT32(64, 0, 4, 32), FA_VARIANT32(64, 1, 4, 32), FA_VARIANT32(128, 0, 4, 32),
+    FA_VARIANT32(128, 1, 4, 32),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -100,6 +118,13 @@ bool head_dim_ok(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
 fa_tile_cfg default_cfg(int /*N*/, int d, int /*causal*/) {
   return d == 256 ? fa_tile_cfg{1, 4, 32} : fa_tile_cfg{1, 8, 64};
 }
+
+// The fp32 path's one configuration: 4 wavefronts, 32-key tiles.
+fa_tile_cfg default_cfg_dt(int N, int d, int causal, int dtype) {
+  return dtype == FA_DTYPE_F32 ? fa_tile_cfg{1, 4, 32} : default_cfg(N, d, causal);
+}
+
+int elem_bytes(int dtype) { return dtype == FA_DTYPE_F32 ? 4 : 2; }
 
 bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
@@ -146,10 +171,13 @@ long long extent_bytes(const long long st[3], int B, int H, int N, int d, int el
   return ((long long)(B - 1) * st[0] + (long long)(H - 1) * st[1] + (long long)(N - 1) * st[2] + d) * elem;
 }
 
-bool strides_ok(const long long st[3], int N, int d) {
+// Strides in elements of `elem` bytes: >= 0, whole 16-byte units, rows at
+// least d long, and (N + 256) rows within 2^31 bytes (one head's buffer range).
+bool strides_ok(const long long st[3], int N, int d, int elem = 2) {
+  const long long unit = 16 / elem;
   for (int i = 0; i < 3; ++i)
-    if (st[i] < 0 || (st[i] & 7) != 0 || st[i] > (1LL << 40)) return false;
-  return st[2] >= d && (long long)(N + 256) * st[2] < (1LL << 30);
+    if (st[i] < 0 || st[i] % unit != 0 || st[i] > (1LL << 40)) return false;
+  return st[2] >= d && (long long)(N + 256) * st[2] * elem < (1LL << 31);
 }
 
 // Host-only checks of a descriptor, in a fixed order; no HIP call is made here.
@@ -157,21 +185,23 @@ int validate_desc(const fa_fwd_desc& a) {
   if (!a.q || !a.k || !a.v || !a.out || !a.lse) return FA_ERR_NULL;
   if (a.B < 1 || a.H < 1 || a.Nq < 1 || a.Nk < 1) return FA_ERR_SHAPE;
   if (!head_dim_ok(a.d)) return FA_ERR_HEAD_DIM;
+  if (a.dtype == FA_DTYPE_F32 && a.d != 64 && a.d != 128) return FA_ERR_HEAD_DIM;
   if ((long long)a.B * a.H > 0x7fffffffLL) return FA_ERR_SHAPE;
-  if (!strides_ok(a.q_stride, a.Nq, a.d) || !strides_ok(a.k_stride, a.Nk, a.d) ||
-      !strides_ok(a.v_stride, a.Nk, a.d) || !strides_ok(a.o_stride, a.Nq, a.d))
+  const int eb = elem_bytes(a.dtype);
+  if (!strides_ok(a.q_stride, a.Nq, a.d, eb) || !strides_ok(a.k_stride, a.Nk, a.d, eb) ||
+      !strides_ok(a.v_stride, a.Nk, a.d, eb) || !strides_ok(a.o_stride, a.Nq, a.d, eb))
     return FA_ERR_STRIDE;
   if (a.lse_stride[0] < 0 || a.lse_stride[1] < 0 || a.lse_stride[0] > (1LL << 40) || a.lse_stride[1] > (1LL << 40))
     return FA_ERR_STRIDE;
   if (!std::isfinite(a.scale) || !(a.scale > 0.f)) return FA_ERR_SCALE;
   if (a.causal != 0 && a.causal != 1) return FA_ERR_ARG;
-  if (a.dtype != FA_DTYPE_BF16 && a.dtype != FA_DTYPE_F16) return FA_ERR_ARG;
+  if (a.dtype != FA_DTYPE_BF16 && a.dtype != FA_DTYPE_F16 && a.dtype != FA_DTYPE_F32) return FA_ERR_ARG;
   auto al = [](const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; };
   if (!al(a.q, 16) || !al(a.k, 16) || !al(a.v, 16) || !al(a.out, 16) || !al(a.lse, 4)) return FA_ERR_ALIGN;
-  const long long qb = extent_bytes(a.q_stride, a.B, a.H, a.Nq, a.d, 2);
-  const long long kb = extent_bytes(a.k_stride, a.B, a.H, a.Nk, a.d, 2);
-  const long long vb = extent_bytes(a.v_stride, a.B, a.H, a.Nk, a.d, 2);
-  const long long ob = extent_bytes(a.o_stride, a.B, a.H, a.Nq, a.d, 2);
+  const long long qb = extent_bytes(a.q_stride, a.B, a.H, a.Nq, a.d, eb);
+  const long long kb = extent_bytes(a.k_stride, a.B, a.H, a.Nk, a.d, eb);
+  const long long vb = extent_bytes(a.v_stride, a.B, a.H, a.Nk, a.d, eb);
+  const long long ob = extent_bytes(a.o_stride, a.B, a.H, a.Nq, a.d, eb);
   const long long lst[3] = {a.lse_stride[0], a.lse_stride[1], 1};
   const long long lb = extent_bytes(lst, a.B, a.H, a.Nq, 1, 4);
   const std::pair<const void*, long long> ins[3] = {{a.q, qb}, {a.k, kb}, {a.v, vb}};
@@ -255,6 +285,7 @@ int default_splits(int B, int H, int Nq, int Nk, int d) {
 int run_splitkv(const fa_fwd_desc& a, int num_splits, void* ws, long long ws_bytes) {
   const int st = validate_desc(a);
   if (st != FA_OK) return st;
+  if (a.dtype == FA_DTYPE_F32) return FA_ERR_ARG;  // no split instantiation of the fp32 kernel
   if (num_splits < 0 || num_splits > 1024) return FA_ERR_ARG;
   const int S = num_splits ? num_splits : default_splits(a.B, a.H, a.Nq, a.Nk, a.d);
   const int S_eff = split_count(a.Nk, S);
@@ -329,7 +360,7 @@ int fa_fwd_cfg(const void* q, const void* k, const void* v, void* out, float* ls
 int fa_fwd_ex(const fa_fwd_desc* desc) {
   if (!desc) return FA_ERR_NULL;
   try {
-    return run_desc(*desc, default_cfg(desc->Nk, desc->d, desc->causal));
+    return run_desc(*desc, default_cfg_dt(desc->Nk, desc->d, desc->causal, desc->dtype));
   } catch (...) {
     return FA_ERR_INTERNAL;
   }
@@ -401,7 +432,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_SHAPE: return "B, H, N must be >= 1, tensors below 2^31 elements and (N + 256) * d below 2^30";
     case FA_ERR_HEAD_DIM: return "head dimension must be 32, 64, 128 or 256";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
-    case FA_ERR_ARG: return "invalid argument (causal must be 0 or 1, dtype bf16 or f16; tile configuration not compiled in)";
+    case FA_ERR_ARG: return "invalid argument (causal must be 0 or 1, dtype bf16, f16 or f32; tile configuration or path not compiled for it)";
     case FA_ERR_ALIGN: return "q, k, v, out must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_ALIAS: return "out/lse overlap an input or each other";
     case FA_ERR_NO_DEVICE: return "no current HIP device, or it is not gfx950";

@@ -109,10 +109,15 @@ int fa_fwd_cfg(const void *q, const void *k, const void *v, void *out, float *ls
  * elements (16 bytes), every row stride >= d, and (N + 256) * row stride < 2^30
  * for each tensor's own N, so that one head stays within 32-bit byte offsets.
  * lse strides >= 0.  Pointers: q, k, v, out 16-byte aligned, lse 4-byte.
- * dtype: FA_DTYPE_BF16 (0, so a zero-initialised descriptor means bfloat16) or
- * FA_DTYPE_F16 (IEEE binary16) for q, k, v and out alike; scores, the softmax
- * statistics and the accumulators are fp32 either way and lse is fp32.  fp16
- * inputs must be finite (|x| <= 65504).
+ * dtype: FA_DTYPE_BF16 (0, so a zero-initialised descriptor means bfloat16),
+ * FA_DTYPE_F16 (IEEE binary16) or FA_DTYPE_F32 (IEEE binary32) for q, k, v and
+ * out alike; scores, the softmax statistics and the accumulators are fp32 in
+ * every case and lse is fp32.  fp16 inputs must be finite (|x| <= 65504).
+ * FA_DTYPE_F32 runs on the fp32 matrix instruction (P stays fp32) for d = 64
+ * or 128 (else FA_ERR_HEAD_DIM) and is not available to fa_fwd_splitkv
+ * (FA_ERR_ARG).  Strides are in elements of the chosen type; the rules below
+ * read "multiple of 16 bytes" for "multiple of 8 elements" and apply the 2^30
+ * bound to bytes / 2.
  * Aliasing (FA_ERR_ALIAS) is judged on each tensor's whole byte extent: out
  * and lse must not overlap q, k, v or each other (inputs may overlap each
  * other, e.g. three views of one packed QKV tensor).
@@ -132,7 +137,7 @@ typedef struct fa_fwd_desc {
 } fa_fwd_desc;
 
 /* Element types of fa_fwd_desc.dtype. */
-enum fa_dtype { FA_DTYPE_BF16 = 0, FA_DTYPE_F16 = 1 };
+enum fa_dtype { FA_DTYPE_BF16 = 0, FA_DTYPE_F16 = 1, FA_DTYPE_F32 = 2 };
 
 int fa_fwd_ex(const fa_fwd_desc *desc);
 

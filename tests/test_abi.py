@@ -53,7 +53,8 @@ def test_variant_table(lib):
             for causal in (0, 1):
                 assert (d, causal, fa.default_cfg(4096, d, causal)) in vs, (dtype, d, causal)
     assert lib.fa_variant_dtype(-1) < 0 and lib.fa_variant_dtype(lib.fa_num_variants()) < 0
-    assert len(fa.variants("bf16")) + len(fa.variants("f16")) == lib.fa_num_variants()
+    assert len(fa.variants("bf16")) + len(fa.variants("f16")) + len(fa.variants("f32")) == lib.fa_num_variants()
+    assert sorted(v[:2] for v in fa.variants("f32")) == [(64, 0), (64, 1), (128, 0), (128, 1)]
 
 
 FAKE = 1 << 20  # 16-byte aligned, never dereferenced: checks fail before any HIP call
@@ -151,7 +152,11 @@ def desc(**kw):
     (dict(v_stride=(8192, -4096, 64)), 11),           # negative
     (dict(o_stride=(8192, 4096, 1 << 24)), 11),       # a head beyond 32-bit offsets
     (dict(lse_stride=(-1, 64)), 11),
-    (dict(scale=0.0), 4), (dict(causal=3), 5), (dict(dtype=2), 5), (dict(dtype=-1), 5),
+    (dict(scale=0.0), 4), (dict(causal=3), 5), (dict(dtype=3), 5), (dict(dtype=-1), 5),
+    (dict(dtype=2, d=32, q_stride=(4096, 2048, 32), k_stride=(4096, 2048, 32), v_stride=(4096, 2048, 32),
+          o_stride=(4096, 2048, 32)), 3),                                   # fp32 takes d = 64 and 128
+    (dict(dtype=2, q_stride=(8192, 4096, 66)), 11),                         # fp32 rows: whole 16-byte units
+    (dict(dtype=2, k_stride=(8192, 4096, 1 << 23)), 11),                    # fp32 head beyond 2^31 bytes
     (dict(d=48), 3),
     (dict(k=2 * FAKE + 8), 6), (dict(lse=5 * FAKE + 2), 6),
     (dict(out=3 * FAKE), 7), (dict(lse=FAKE + 256), 7),
@@ -177,6 +182,10 @@ def test_desc_valid_layouts_reach_the_device_check(lib):
     for d in (32, 256):                                     # the other head dims, both element types
         for dt in (0, 1):
             assert fa.fa_fwd_ex_ptr(desc(d=d, dtype=dt)) == 8
+    for d in (64, 128):                                     # fp32; a 4-element (16-byte) row pitch is legal
+        st = (2 * 64 * (d + 4), 64 * (d + 4), d + 4)
+        assert fa.fa_fwd_ex_ptr(desc(d=d, dtype=2, q_stride=st, k_stride=st, v_stride=st, o_stride=st,
+                                     out=8 * FAKE)) == 8
     assert fa.fa_fwd_ex_ptr(desc(B=B, H=H, Nq=N, Nk=N, q_stride=bnhd, k_stride=bnhd, v_stride=bnhd,
                                  o_stride=bnhd, out=8 * FAKE)) == 8
     packed = (N * 3 * H * d, d, 3 * H * d)  # [B, N, 3, H, d]: q, k, v interleaved
@@ -202,6 +211,11 @@ def test_splitkv_workspace_and_default_splits(lib):
 
 
 WS = 64 * FAKE  # 256-byte aligned, far from the tensors
+
+
+def test_splitkv_rejects_fp32(lib):
+    d = desc(dtype=2)
+    assert lib.fa_fwd_splitkv(ctypes.byref(d), 2, ctypes.c_void_p(WS), ctypes.c_longlong(1 << 30)) == 5
 
 
 @pytest.mark.parametrize("args,code", [

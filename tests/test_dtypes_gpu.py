@@ -1,6 +1,6 @@
-"""GPU parity of the other element type and head dims (fp16 inputs; d = 32 and
-256) against the fp64 CPU oracle, through fa_fwd_ex (desc.dtype) and the split
-path; fa_fwd (bfloat16) at d = 32 and 256."""
+"""GPU parity of the other element types and head dims (fp16 inputs; d = 32 and
+256; fp32 inputs on the fp32 kernel) against the fp64 CPU oracle, through
+fa_fwd_ex (desc.dtype) and the split path; fa_fwd (bfloat16) at d = 32 and 256."""
 import numpy as np
 import pytest
 
@@ -110,3 +110,68 @@ def test_d256_longer_head(dtype):
     q, k, v = qkv(8400, 1, 2, 2048, 2048, 256, dtype)
     run = lambda a, b, c: fa.fa_fwd_ex(a, b, c, scale=fp32_scale(256), causal=True)
     check(q, k, v, 1, dtype, "%s d=256 N=2048 causal" % dtype, run)
+
+
+# ---------------------------------------------------------------- fp32 inputs
+# fp32 products and sums: scores carry about sqrt(d) * 2^-24 * |s| of error,
+# O about sqrt(N) * 2^-24 * |O| more, and v_exp_f32 about 1 ulp: below 1e-5 for
+# these inputs.  Bars: max |dO| <= 1e-4, mean <= 1e-5, LSE 1e-5 relative.
+F32_MAX, F32_MEAN, F32_LSE = 1e-4, 1e-5, 1e-5
+
+
+def f32_device(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda:0")
+
+
+def check_f32(q, k, v, causal, label, run):
+    import torch
+    d = q.shape[-1]
+    out, lse = run(f32_device(q), f32_device(k), f32_device(v))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_rows_f32(q, k, v, fp32_scale(d), causal)
+    o = out.contiguous().cpu().numpy().astype(np.float64).reshape(-1, d)
+    L = lse.contiguous().cpu().numpy().astype(np.float64).reshape(-1)
+    err = np.abs(o - o_ref)
+    lerr = (np.abs(L - l_ref) / np.maximum(1.0, np.abs(l_ref))).max()
+    import sys
+    print("[parity] %s max|dO|=%.3e mean|dO|=%.3e lse=%.3e" % (label, err.max(), err.mean(), lerr),
+          file=sys.stderr, flush=True)
+    assert np.all(np.isfinite(o))
+    assert err.max() <= F32_MAX and err.mean() <= F32_MEAN and lerr <= F32_LSE, (err.max(), err.mean(), lerr)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("Nq,Nk", [(300, 300), (1, 777), (200, 77), (1000, 1000)])
+def test_f32_inputs(d, causal, Nq, Nk):
+    import flashattention_forward_fa2_amd as fa
+    q, k, v = qkv(8500 + d + Nq + causal, 2, 2, Nq, Nk, d, "f32")
+    run = lambda a, b, c: fa.fa_fwd_ex(a, b, c, scale=fp32_scale(d), causal=bool(causal))
+    check_f32(q, k, v, causal, "f32 d=%d c=%d Nq=%d Nk=%d" % (d, causal, Nq, Nk), run)
+
+
+def test_f32_strided_views_and_peaked_scores():
+    """[B, N, H, d] fp32 views with scaled scores of sigma 16."""
+    import flashattention_forward_fa2_amd as fa
+    d = 128
+    q, k, v = qkv(8600, 2, 3, 400, 400, d, "f32", sigma=4.0)
+    def run(a, b, c):
+        a, b, c = (t.permute(0, 2, 1, 3).contiguous().transpose(1, 2) for t in (a, b, c))
+        return fa.fa_fwd_ex(a, b, c, scale=fp32_scale(d), causal=True)
+    check_f32(q, k, v, 1, "f32 strided peaked", run)
+
+
+def test_f32_long_head_sampled_rows():
+    """B1-H4-N4096 d128 causal in fp32, every row of two heads."""
+    import torch
+    import flashattention_forward_fa2_amd as fa
+    d = 128
+    q, k, v = qkv(8700, 1, 4, 4096, 4096, d, "f32")
+    out, lse = fa.fa_fwd_ex(f32_device(q), f32_device(k), f32_device(v), scale=fp32_scale(d), causal=True)
+    torch.cuda.synchronize()
+    rows = np.arange(2 * 4096, dtype=np.int64)
+    o_ref, l_ref = oracle.attention_rows_f32(q, k, v, fp32_scale(d), True, rows)
+    o = out.cpu().numpy().astype(np.float64).reshape(-1, d)[rows]
+    assert np.abs(o - o_ref).max() <= F32_MAX
+    assert (np.abs(lse.cpu().numpy().reshape(-1)[rows] - l_ref) / np.maximum(1, np.abs(l_ref))).max() <= F32_LSE
