@@ -178,3 +178,13 @@ def test_errors_do_not_launch():
     assert st == 4
     torch.cuda.synchronize()
     assert torch.all(out == 3.0) and torch.all(lse == 3.0)
+
+
+@pytest.mark.parametrize("N,d,causal", [(1 << 19, 64, 1), ((1 << 20) + 17, 128, 0)])
+def test_very_long_single_head(N, d, causal):
+    """One head of half a million / a million keys: byte offsets inside a head
+    approach the 32-bit range the kernels use (N * d * 2 up to 2^28), and the
+    last tile is ragged.  Sampled rows, including the last ones."""
+    q, k, v = random_qkv(7700 + d, 1, 1, N, d)
+    rows = np.array([0, 1, 63, 64, 4095, N // 2, N - 65, N - 2, N - 1], dtype=np.int64)
+    check_rows(q, k, v, fp32_scale(d), causal, rows=rows, label="long N=%d d=%d causal=%d" % (N, d, causal))
