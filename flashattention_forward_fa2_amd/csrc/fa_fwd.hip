@@ -99,6 +99,10 @@ const Variant kVariants[] = {
     FA_VARIANTS_SMALL(FA_VARIANT16, 64, 0), FA_VARIANTS_SMALL(FA_VARIANT16, 64, 1),
     FA_VARIANTS_SMALL(FA_VARIANT16, 128, 0), FA_VARIANTS_SMALL(FA_VARIANT16, 128, 1),
     FA_VARIANT16(256, 0, 1, 4, 32), FA_VARIANT16(256, 1, 1, 4, 32),
+    // one wavefront of 32 queries: the split path's tile for decoding (Nq <= 32)
+    FA_VARIANT(64, 0, 1, 1, 64), FA_VARIANT(64, 1, 1, 1, 64), FA_VARIANT(128, 0, 1, 1, 32),
+    FA_VARIANT(128, 1, 1, 1, 32), FA_VARIANT16(64, 0, 1, 1, 64), FA_VARIANT16(64, 1, 1, 1, 64),
+    FA_VARIANT16(128, 0, 1, 1, 32), FA_VARIANT16(128, 1, 1, 1, 32),
     FA_VARIANT32(64, 0, 4, 32), FA_VARIANT32(64, 1, 4, 32), FA_VARIANT32(128, 0, 4, 32),
     FA_VARIANT32(128, 1, 4, 32),
 };
@@ -266,10 +270,13 @@ long long split_workspace(int B, int H, int Nq, int d, int S_eff) {
   return (long long)S_eff * B * H * Nq * (d + 1) * 4;
 }
 
-// Tile configuration of the split path: short query ranges (decoding, short
-// prompts) take the 4-wave, 128-query tile, so fewer MFMA rows are padding
-// (d = 256 has 4-wave tiles only).
+// Tile configuration of the split path: short query ranges take smaller
+// workgroups so fewer MFMA rows are padding -- one wavefront of 32 queries when
+// Nq <= 32 (decoding: 32 KB of LDS each, so five fit on a CU and more key
+// streams are in flight), the 4-wave, 128-query tile when Nq <= 128 (d = 32
+// and 256 have the 4-wave tiles only).
 fa_tile_cfg split_cfg(int Nq, int Nk, int d, int causal) {
+  if (Nq <= 32 && (d == 64 || d == 128)) return fa_tile_cfg{1, 1, d == 128 ? 32 : 64};
   return Nq <= 128 && d != 256 ? fa_tile_cfg{1, 4, 64} : default_cfg(Nk, d, causal);
 }
 
@@ -277,8 +284,10 @@ fa_tile_cfg split_cfg(int Nq, int Nk, int d, int causal) {
 int default_splits(int B, int H, int Nq, int Nk, int d) {
   const fa_tile_cfg c = split_cfg(Nq, Nk, d, 0);
   const long long wgs = (long long)B * H * ((Nq + c.waves * c.qb * 32 - 1) / (c.waves * c.qb * 32));
-  long long s = (512 + wgs - 1) / wgs;       // about two workgroups per CU
-  s = std::min<long long>(s, std::max(1, Nk / 256));  // at least 256 keys per split
+  long long s = (512 + wgs - 1) / wgs;       // about 512 workgroups
+  // at least 256 keys per split (512 for single-wavefront workgroups, whose
+  // per-split setup weighs more against their short key streams)
+  s = std::min<long long>(s, std::max(1, Nk / (c.waves == 1 ? 512 : 256)));
   return (int)std::max<long long>(1, std::min<long long>(s, 1024));
 }
 

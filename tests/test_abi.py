@@ -204,7 +204,8 @@ def test_splitkv_workspace_and_default_splits(lib):
     assert fa.splitkv_workspace_bytes(1, 1, 1, 100, 64, 16) == 2 * 65 * 4
     assert fa.splitkv_default_splits(1, 8, 1024, 1024, 64) == 4      # 32 workgroups, >= 256 keys per split
     assert fa.splitkv_default_splits(1, 32, 1, 32768, 128) == 16     # decode: 32 workgroups -> 16 splits
-    assert fa.splitkv_default_splits(4, 32, 1, 8192, 128) == 4       # 128 workgroups of 128 queries
+    assert fa.splitkv_default_splits(4, 32, 1, 8192, 128) == 4       # 128 single-wavefront workgroups
+    assert fa.splitkv_default_splits(4, 8, 1, 4096, 64) == 8         # >= 512 keys per single-wave split
     assert fa.splitkv_default_splits(4, 8, 4096, 4096, 64) == 1      # 512 workgroups already
     with pytest.raises(fa.FaError):
         fa.splitkv_workspace_bytes(1, 1, 1, 1, 96, 1)
