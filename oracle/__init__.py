@@ -67,6 +67,8 @@ def _load():
                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                 ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+            lib.oracle_attention_bwd_dt.restype = ctypes.c_int
+            lib.oracle_attention_bwd_dt.argtypes = lib.oracle_attention_bwd.argtypes + [ctypes.c_int]
             lib.oracle_num_threads.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -136,19 +138,21 @@ def attention_rows_f32(q, k, v, scale: float, causal: bool, rows=None):
     return out, lse
 
 
-def attention_bwd(q, k, v, dout, scale: float, causal: bool):
+def attention_bwd(q, k, v, dout, scale: float, causal: bool, dtype: str = "bf16"):
     """Gradients (dq, dk, dv) of sum(dout * out) in fp64, each [B, H, N, d].
 
-    ``q, k, v, dout``: uint16 bfloat16 bit arrays [B, H, N, d] (square heads).
-    Follows ``oracle_attention_bwd`` in ``oracle.c``.
+    ``q, k, v, dout``: uint16 bit arrays [B, H, N, d] (square heads) of bfloat16
+    or (``dtype="f16"``) fp16 values.  Follows ``oracle_attention_bwd_dt`` in
+    ``oracle.c``.
     """
     arrs = [np.ascontiguousarray(a, dtype=np.uint16) for a in (q, k, v, dout)]
     if arrs[0].ndim != 4 or any(a.shape != arrs[0].shape for a in arrs):
         raise ValueError("q, k, v, dout must share one [B, H, N, d] shape")
     B, H, N, d = arrs[0].shape
     dq, dk, dv = (np.empty((B, H, N, d), dtype=np.float64) for _ in range(3))
-    rc = _load().oracle_attention_bwd(*(a.ctypes.data for a in arrs), B, H, N, d, float(scale),
-                                      int(bool(causal)), dq.ctypes.data, dk.ctypes.data, dv.ctypes.data)
+    rc = _load().oracle_attention_bwd_dt(*(a.ctypes.data for a in arrs), B, H, N, d, float(scale),
+                                         int(bool(causal)), dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
+                                         DTYPES[dtype])
     if rc != 0:
         raise RuntimeError("oracle_attention_bwd failed with code %d" % rc)
     return dq, dk, dv

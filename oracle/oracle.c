@@ -233,16 +233,18 @@ int oracle_attention_rows(const uint16_t *q, const uint16_t *k, const uint16_t *
  *   dS_ij = P_ij (dP_ij - D_i)
  *   dQ_i  = scale sum_j dS_ij k_j,    dK_j = scale sum_i dS_ij q_i
  *
- * Square heads, contiguous [B, H, N, d] bfloat16 inputs; dq, dk, dv are
+ * Square heads, contiguous [B, H, N, d] inputs of bfloat16 (dtype 0) or fp16
+ * (dtype 1); dq, dk, dv are
  * B*H*N*d doubles.  One score row at a time (no N x N buffer): the dQ row is
  * finished per query, dK and dV accumulate over queries; each head is one
  * OpenMP task, so accumulation order is fixed.  Returns 0, 1 on a bad argument,
  * 2 if scratch memory is exhausted.
  */
-int oracle_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
-                         int64_t B, int64_t H, int64_t N, int64_t d, double scale, int causal,
-                         double *dq, double *dk, double *dv) {
+int oracle_attention_bwd_dt(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                            int64_t B, int64_t H, int64_t N, int64_t d, double scale, int causal,
+                            double *dq, double *dk, double *dv, int dtype) {
   if (!q || !k || !v || !dout || !dq || !dk || !dv) return 1;
+  if (dtype != 0 && dtype != 1) return 1;
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 1;
   int failed = 0;
 #pragma omp parallel
@@ -264,14 +266,14 @@ int oracle_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v
         for (int64_t i = 0; i < N; ++i) {
           const int64_t nkeys = causal ? i + 1 : N;
           for (int64_t c = 0; c < d; ++c) {
-            qi[c] = oracle_bf16_to_f64(qh[i * d + c]);
-            gi[c] = oracle_bf16_to_f64(gh[i * d + c]);
+            qi[c] = oracle_to_f64(qh[i * d + c], dtype);
+            gi[c] = oracle_to_f64(gh[i * d + c], dtype);
           }
           /* probabilities of row i (the forward's definition) */
           double m = -INFINITY;
           for (int64_t j = 0; j < nkeys; ++j) {
             double acc = 0.0;
-            for (int64_t c = 0; c < d; ++c) acc += qi[c] * oracle_bf16_to_f64(kh[j * d + c]);
+            for (int64_t c = 0; c < d; ++c) acc += qi[c] * oracle_to_f64(kh[j * d + c], dtype);
             p[j] = scale * acc;
             if (p[j] > m) m = p[j];
           }
@@ -282,7 +284,7 @@ int oracle_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v
           double D = 0.0;
           for (int64_t j = 0; j < nkeys; ++j) {
             double acc = 0.0;
-            for (int64_t c = 0; c < d; ++c) acc += gi[c] * oracle_bf16_to_f64(vh[j * d + c]);
+            for (int64_t c = 0; c < d; ++c) acc += gi[c] * oracle_to_f64(vh[j * d + c], dtype);
             dp[j] = acc;
             D += p[j] * acc;
           }
@@ -291,7 +293,7 @@ int oracle_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v
             const double ds = p[j] * (dp[j] - D);
             for (int64_t c = 0; c < d; ++c) {
               dvh[j * d + c] += p[j] * gi[c];
-              dqh[i * d + c] += scale * ds * oracle_bf16_to_f64(kh[j * d + c]);
+              dqh[i * d + c] += scale * ds * oracle_to_f64(kh[j * d + c], dtype);
               dkh[j * d + c] += scale * ds * qi[c];
             }
           }
@@ -304,4 +306,11 @@ int oracle_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v
     free(gi);
   }
   return failed ? 2 : 0;
+}
+
+/* bfloat16 inputs. */
+int oracle_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                         int64_t B, int64_t H, int64_t N, int64_t d, double scale, int causal,
+                         double *dq, double *dk, double *dv) {
+  return oracle_attention_bwd_dt(q, k, v, dout, B, H, N, d, scale, causal, dq, dk, dv, 0);
 }

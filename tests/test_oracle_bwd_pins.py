@@ -67,3 +67,30 @@ def test_zero_upstream_gradient_gives_zero():
     z = np.zeros_like(q)
     for grad in oracle.attention_bwd(q, k, v, z, 0.3, True):
         assert not np.any(grad)
+
+
+@pytest.mark.parametrize("N,d,causal", [(6, 4, False), (7, 8, True)])
+def test_f16_gradients_match_finite_differences(N, d, causal):
+    """fp16 inputs: the oracle decodes them as IEEE binary16 (values a bfloat16
+    reading would get wrong) and its gradients match central differences."""
+    from inputs import f16_bits_to_f64
+    q, k, v = random_qkv(1200 + N + d, 1, 1, N, d, sigma_qk=1.5, dtype="f16")
+    g, _, _ = random_qkv(1250 + N, 1, 1, N, d, dtype="f16")
+    scale = float(np.float32(1 / math.sqrt(d)))
+    dq, dk, dv = oracle.attention_bwd(q, k, v, g, scale, causal, dtype="f16")
+    Q, K, V, G = (f16_bits_to_f64(a)[0, 0] for a in (q, k, v, g))
+
+    def f(Q_, K_, V_):
+        return float(np.sum(G * forward_np(Q_, K_, V_, scale, causal)))
+
+    eps = 1e-6
+    for name, X, grad in (("q", Q, dq), ("k", K, dk), ("v", V, dv)):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(*X.shape):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[idx] += eps
+            Xm[idx] -= eps
+            args_p = {"q": (Xp, K, V), "k": (Q, Xp, V), "v": (Q, K, Xp)}[name]
+            args_m = {"q": (Xm, K, V), "k": (Q, Xm, V), "v": (Q, K, Xm)}[name]
+            num[idx] = (f(*args_p) - f(*args_m)) / (2 * eps)
+        assert np.allclose(grad[0, 0], num, atol=1e-7, rtol=1e-6), name
