@@ -277,34 +277,56 @@ BWD_METRIC = "attention bwd TFLOP/s (bf16, dQ dK dV; 2.5x the forward's FLOPs) a
 def main_bwd(args):
     """The backward pass (three kernels per call) over the workload's modes:
     out, LSE and dO are computed / drawn before the timed region; one step is
-    one fa_bwd call per mode.  FLOPs are the 5 matrix products of the chain
-    rule, 10*B*H*N^2*d (halved for causal); the dQ pass's recomputation of S and
-    dP is not counted."""
+    one backward call per mode (fa_bwd, or fa_bwd_ex for fp16 or the [B, N, H, d]
+    layout).  FLOPs are the 5 matrix products of the chain rule,
+    10*B*H*N^2*d (halved for causal); the dQ pass's recomputation of S and dP
+    is not counted."""
     import torch
     import flashattention_forward_fa2_amd as fa
     import inputs
 
+    if args.dtype == "f32":
+        print("the backward takes bf16 or f16 inputs", file=sys.stderr)
+        sys.exit(2)
     fa.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = inputs.WORKLOADS[args.workload]
+    w = dict(inputs.WORKLOADS[args.workload])
+    if args.headdim:
+        w["d"] = args.headdim
+        w["name"] = re.sub(r"-d\d+", "-d%d" % args.headdim, w["name"])
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
     modes = list(w["modes"]) if args.workload != 3 else [0, 1]
     if args.only:
         modes = [c for c in modes if c == (args.only == "causal")]
     scale = inputs.default_scale(d)
-    q_bits, k_bits, v_bits = inputs.make_qkv(args.workload)
-    g_bits = inputs.normal_bf16(inputs.workload_seed(args.workload, 4), B * H * N * d).reshape(B, H, N, d)
-    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q_bits, k_bits, v_bits = inputs.make_qkv(args.workload, d=d, dtype=args.dtype)
+    g_bits = inputs.normal_bits(inputs.workload_seed(args.workload, 4), B * H * N * d,
+                                dtype=args.dtype).reshape(B, H, N, d)
+    tdt = torch.float16 if args.dtype == "f16" else torch.bfloat16
+    general = args.layout == "bnhd" or args.dtype != "bf16"
+    if args.layout == "bnhd":
+        # stored [B, N, H, d]; the kernels see [B, H, N, d] views with row stride H*d
+        to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3)).view(np.int16)).view(
+            tdt).to(dev).transpose(1, 2)
+        new = lambda: torch.empty((B, N, H, d), dtype=tdt, device=dev).transpose(1, 2)
+    else:
+        to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(tdt).to(dev)
+        new = lambda: torch.empty((B, H, N, d), dtype=tdt, device=dev)
     q, k, v, dout = (to_dev(a) for a in (q_bits, k_bits, v_bits, g_bits))
     stream = torch.cuda.current_stream(dev)
-    fw = {c: fa.fa_fwd(q, k, v, scale=scale, causal=bool(c), stream=stream) for c in modes}
-    grads = {c: tuple(torch.empty_like(q) for _ in range(3)) for c in modes}
+    fwd = fa.fa_fwd_ex if general else fa.fa_fwd
+    fw = {}
+    for c in modes:
+        o = new()
+        fw[c] = fwd(q, k, v, scale=scale, causal=bool(c), out=o, stream=stream)
+    grads = {c: tuple(new() for _ in range(3)) for c in modes}
     ws = torch.empty(fa.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    bwd = fa.fa_bwd_ex if general else fa.fa_bwd
 
     def launch(c):
-        fa.fa_bwd(q, k, v, fw[c][0], fw[c][1], dout, scale=scale, causal=bool(c), dq=grads[c][0], dk=grads[c][1],
-                  dv=grads[c][2], workspace=ws, stream=stream)
+        bwd(q, k, v, fw[c][0], fw[c][1], dout, scale=scale, causal=bool(c), dq=grads[c][0], dk=grads[c][1],
+            dv=grads[c][2], workspace=ws, stream=stream)
 
     for _ in range(max(1, args.warmup)):
         for c in modes:
@@ -340,15 +362,16 @@ def main_bwd(args):
             call_ms_min=round(float(ms.min()), 5), tflops=round(tf, 2), frac_of_peak=round(tf / PEAK_BF16_TFLOPS, 4))
     dom_c = max(modes, key=lambda c: per_mode["causal" if c else "noncausal"]["call_ms_avg"])
     dom = per_mode["causal" if dom_c else "noncausal"]
+    traffic = None if general else measured_traffic_bwd(B, H, N, d, dom_c)
     roofline = dict(bound="mfma", achieved=dom["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=dom["frac_of_peak"], traffic=measured_traffic_bwd(B, H, N, d, dom_c),
-                    kernel="fa_bwd (pre + dK/dV + dQ kernels) d=%d causal=%d" % (d, dom_c),
+                    frac=dom["frac_of_peak"], traffic=traffic,
+                    kernel="%s (pre + dK/dV + dQ kernels) d=%d causal=%d" % (bwd.__name__, d, dom_c),
                     flops_per_launch=bflops(dom_c))
 
     cpu = None
     if not args.no_cpu_baseline and 2.5 * flops(1, 1, N, d, max(modes)) <= 300e9:
         import oracle
-        from inputs import bf16_bits_to_f64
+        from inputs import bits_to_f64
         # one whole head per oracle thread, within ~300 GFLOP of fp64 work
         nh = min(B * H, max(1, oracle.num_threads()), int(300e9 // (2.5 * flops(1, 1, N, d, max(modes)) * len(modes))))
         heads = [(i // H, i % H) for i in range(0, B * H, max(1, (B * H) // nh))][:nh]
@@ -356,13 +379,14 @@ def main_bwd(args):
         total_flops, total_s, parity = 0.0, 0.0, {}
         for c in modes:
             t0 = time.perf_counter()
-            ref = oracle.attention_bwd(sel(q_bits), sel(k_bits), sel(v_bits), sel(g_bits), scale, bool(c))
+            ref = oracle.attention_bwd(sel(q_bits), sel(k_bits), sel(v_bits), sel(g_bits), scale, bool(c),
+                                       dtype=args.dtype)
             total_s += time.perf_counter() - t0
             total_flops += 2.5 * flops(1, len(heads), N, d, c)
             errs = {}
             for name, g, r in zip(("dq", "dk", "dv"), grads[c], ref):
-                gb = sel(g.view(torch.int16).cpu().numpy().view(np.uint16))
-                e = np.abs(bf16_bits_to_f64(gb) - r)
+                gb = sel(g.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+                e = np.abs(bits_to_f64(gb, args.dtype) - r)
                 errs[name] = dict(max_rel=float(e.max() / np.abs(r).max()),
                                   rms_rel=float(np.sqrt(np.mean(e ** 2)) / np.sqrt(np.mean(r ** 2))))
             parity["causal" if c else "noncausal"] = errs
@@ -375,8 +399,10 @@ def main_bwd(args):
     rec = {
         "metric": BWD_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "%s backward %s" % (w["name"], "+".join("causal" if c else "non-causal" for c in modes)),
+        "scaling": "weak", "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
+        "config": {"workload": "%s%s%s backward %s" % (w["name"], " fp16" if args.dtype == "f16" else "",
+                                                       " [B,N,H,d] strided" if args.layout == "bnhd" else "",
+                                                       "+".join("causal" if c else "non-causal" for c in modes)),
                    "B": B, "H": H, "N": N, "d": d, "scale": scale, "flops_per_step": step_flops, "modes": per_mode},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -16,11 +16,12 @@ from .buildlib import LIB, build  # noqa: F401
 __all__ = ["fa_fwd", "fa_fwd_ptr", "fa_fwd_cfg", "fa_fwd_ex", "fa_fwd_ex_ptr", "fa_fwd_splitkv",
            "splitkv_workspace_bytes", "splitkv_default_splits", "FwdDesc", "FaError", "strerror",
            "version", "default_cfg", "variants", "load_library", "EXPORTED_SYMBOLS", "fa_bwd", "fa_bwd_ptr",
-           "bwd_workspace_bytes"]
+           "bwd_workspace_bytes", "fa_bwd_ex", "fa_bwd_ex_ptr", "BwdDesc"]
 
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_cfg", "fa_fwd_ex", "fa_fwd_ex_cfg", "fa_fwd_splitkv",
                     "fa_splitkv_workspace_bytes", "fa_splitkv_default_splits", "fa_default_cfg", "fa_num_variants",
-                    "fa_variant", "fa_variant_dtype", "fa_strerror", "fa_version", "fa_bwd", "fa_bwd_workspace_bytes")
+                    "fa_variant", "fa_variant_dtype", "fa_strerror", "fa_version", "fa_bwd", "fa_bwd_ex",
+                    "fa_bwd_workspace_bytes")
 
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD_DIM", 4: "FA_ERR_SCALE",
           5: "FA_ERR_ARG", 6: "FA_ERR_ALIGN", 7: "FA_ERR_ALIAS", 8: "FA_ERR_NO_DEVICE",
@@ -54,6 +55,20 @@ class FwdDesc(ctypes.Structure):
                 ("lse_stride", _LL2),
                 ("scale", ctypes.c_float), ("causal", ctypes.c_int), ("stream", ctypes.c_void_p),
                 ("dtype", ctypes.c_int)]
+
+
+class BwdDesc(ctypes.Structure):
+    """Mirror of ``fa_bwd_desc`` (include/fa_bwd.h): strided, bf16 or fp16 backward."""
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("dout", ctypes.c_void_p),
+                ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+                ("B", ctypes.c_int), ("H", ctypes.c_int), ("N", ctypes.c_int), ("d", ctypes.c_int),
+                ("q_stride", _LL3), ("k_stride", _LL3), ("v_stride", _LL3), ("o_stride", _LL3),
+                ("do_stride", _LL3), ("dq_stride", _LL3), ("dk_stride", _LL3), ("dv_stride", _LL3),
+                ("lse_stride", _LL2),
+                ("scale", ctypes.c_float), ("causal", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_longlong),
+                ("stream", ctypes.c_void_p)]
 
 
 DTYPE_BF16, DTYPE_F16, DTYPE_F32 = 0, 1, 2
@@ -117,6 +132,8 @@ def load_library():
             lib.fa_bwd_workspace_bytes.restype = ctypes.c_longlong
             lib.fa_bwd.argtypes = [_P] * 9 + [_I, _I, _I, _I, ctypes.c_float, _I, _P, ctypes.c_longlong, _P]
             lib.fa_bwd.restype = _I
+            lib.fa_bwd_ex.argtypes = [ctypes.POINTER(BwdDesc)]
+            lib.fa_bwd_ex.restype = _I
             _lib = lib
     return _lib
 
@@ -361,4 +378,61 @@ def fa_bwd(q, k, v, out, lse, dout, scale: float | None = None, causal: bool = F
                     grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(), B, H, N, d, scale, causal,
                     workspace.data_ptr(), nbytes, _stream_handle(stream, q.device))
     _check(st)
+    return tuple(grads)
+
+
+def fa_bwd_ex_ptr(desc: BwdDesc) -> int:
+    """Raw descriptor call of ``fa_bwd_ex``; returns the status code (does not raise)."""
+    return int(load_library().fa_bwd_ex(ctypes.byref(desc)))
+
+
+def fa_bwd_ex(q, k, v, out, lse, dout, scale: float | None = None, causal: bool = False, dq=None, dk=None,
+              dv=None, workspace=None, stream=None):
+    """Attention backward on strided bf16 or fp16 views (square heads).
+
+    ``q, k, v, out, dout`` are [B, H, N, d] views of one dtype with a contiguous
+    last dimension (a [B, N, H, d] tensor is passed as ``t.transpose(1, 2)``),
+    ``lse`` a [B, H, N] fp32 view with unit row stride.  ``dq, dk, dv``
+    (default: new contiguous tensors) are [B, H, N, d] views of that dtype.
+    Returns ``(dq, dk, dv)``; enqueued on ``stream``, no synchronisation.
+    """
+    import torch
+    if q.dim() != 4 or any(t.dim() != 4 or t.shape != q.shape for t in (k, v, out, dout)):
+        raise ValueError("q, k, v, out, dout must share one [B, H, N, d] shape")
+    et = q.dtype
+    if et not in (torch.bfloat16, torch.float16):
+        raise ValueError("the backward takes bfloat16 or float16 tensors")
+    for t in (q, k, v, out, dout):
+        if t.dtype != et or not t.is_cuda or t.stride(3) != 1:
+            raise ValueError("q, k, v, out, dout must be device views of one dtype with a contiguous last dimension")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or lse.stride(2) != 1:
+        raise ValueError("lse must be an fp32 [B, H, N] view with unit row stride")
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    grads = []
+    for g in (dq, dk, dv):
+        if g is None:
+            g = torch.empty((B, H, N, d), dtype=et, device=q.device)
+        if g.shape != q.shape or g.dtype != et or g.stride(3) != 1:
+            raise ValueError("dq, dk, dv must be [B, H, N, d] views of q's dtype with a contiguous last dimension")
+        grads.append(g)
+    need = bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    desc = BwdDesc()
+    desc.q, desc.k, desc.v, desc.out, desc.lse, desc.dout = (t.data_ptr() for t in (q, k, v, out, lse, dout))
+    desc.dq, desc.dk, desc.dv = (g.data_ptr() for g in grads)
+    desc.B, desc.H, desc.N, desc.d = B, H, N, d
+    for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", out), ("do_stride", dout),
+                    ("dq_stride", grads[0]), ("dk_stride", grads[1]), ("dv_stride", grads[2])):
+        setattr(desc, name, _LL3(*t.stride()[:3]))
+    desc.lse_stride = _LL2(*lse.stride()[:2])
+    desc.scale = float(scale)
+    desc.causal = int(bool(causal))
+    desc.dtype = DTYPE_F16 if et == torch.float16 else DTYPE_BF16
+    desc.workspace = workspace.data_ptr()
+    desc.workspace_bytes = workspace.numel() * workspace.element_size()
+    desc.stream = _stream_handle(stream, q.device)
+    _check(fa_bwd_ex_ptr(desc))
     return tuple(grads)

@@ -1,5 +1,6 @@
 // C ABI of the gfx950 FlashAttention-2 backward: argument checks and the three
-// launches (D / LSE preprocessing, dK and dV, dQ).  Declared in include/fa_bwd.h.
+// launches (D / LSE preprocessing, dK and dV, dQ), for bf16 or fp16 tensors,
+// contiguous or strided.  Declared in include/fa_bwd.h.
 #include "fa_bwd.h"
 
 #include <hip/hip_runtime.h>
@@ -59,67 +60,122 @@ int check_sizes(int B, int H, int N, int d) {
 
 long long workspace_bytes(int B, int H, int N) { return 8LL * B * H * N; }
 
-struct Args {
-  const void *q, *k, *v, *out;
-  const float* lse;
-  const void* dout;
-  void *dq, *dk, *dv;
-  int B, H, N, d;
-  float scale;
-  int causal;
-  void* ws;
-  long long ws_bytes;
-  void* stream;
+// Byte extent of a strided [B, H, N, d] tensor of 2-byte elements (d = 1, elem
+// = 4 for lse): from its base to one past its last element.
+long long extent_bytes(const long long st[3], int B, int H, int N, int d, int elem) {
+  return ((long long)(B - 1) * st[0] + (long long)(H - 1) * st[1] + (long long)(N - 1) * st[2] + d) * elem;
+}
+
+// Strides in 2-byte elements: >= 0, whole 16-byte units, rows at least d long,
+// and (N + 256) rows within 2^31 bytes (one head's buffer range).
+bool strides_ok(const long long st[3], int N, int d) {
+  for (int i = 0; i < 3; ++i)
+    if (st[i] < 0 || st[i] % 8 != 0 || st[i] > (1LL << 40)) return false;
+  return st[2] >= d && (long long)(N + 256) * st[2] * 2 < (1LL << 31);
+}
+
+// A tensor's bytes for the alias checks: the extent [base, base + extent) and,
+// for a strided 16-bit view, its byte row stride rs and the bytes one row of all
+// heads spans (row_span), with batch stride sb.  rs = 0: extent only.
+struct Footprint {
+  uintptr_t base;
+  long long extent, sb, rs, row_span;
 };
 
-// Host-only checks, in the documented order; no HIP call is made here.
-int validate(const Args& a) {
-  if (!a.q || !a.k || !a.v || !a.out || !a.lse || !a.dout || !a.dq || !a.dk || !a.dv || !a.ws) return FA_ERR_NULL;
-  const int st = check_sizes(a.B, a.H, a.N, a.d);
-  if (st != FA_OK) return st;
+Footprint footprint(const void* p, const long long st[3], int B, int H, int N, int d) {
+  return {reinterpret_cast<uintptr_t>(p), extent_bytes(st, B, H, N, d, 2), st[0] * 2, st[2] * 2,
+          ((long long)(H - 1) * st[1] + d) * 2};
+}
+
+// False only when the two byte sets are provably disjoint: their extents do not
+// meet, or both are views with one row stride rs, batch strides that are
+// multiples of rs and all heads of a row within rs bytes, so that every byte of
+// a view lies in the interval [base mod rs, base mod rs + row_span) modulo rs;
+// disjoint intervals then mean disjoint views.  This admits dq, dk, dv written
+// interleaved into one packed [B, N, 3, H, d] buffer.
+bool may_overlap(const Footprint& a, const Footprint& b) {
+  if (!overlaps(reinterpret_cast<const void*>(a.base), (size_t)a.extent, reinterpret_cast<const void*>(b.base),
+                (size_t)b.extent))
+    return false;
+  const long long rs = a.rs;
+  if (rs <= 0 || b.rs != rs || a.sb % rs != 0 || b.sb % rs != 0 || a.row_span > rs || b.row_span > rs) return true;
+  const long long ra = (long long)(a.base % (uintptr_t)rs), rb = (long long)(b.base % (uintptr_t)rs);
+  const long long ab = ((rb - ra) % rs + rs) % rs, ba = ((ra - rb) % rs + rs) % rs;
+  return !(ab >= a.row_span && ba >= b.row_span);
+}
+
+bool contiguous(const long long st[3], int H, int N, int d) {
+  return st[2] == d && st[1] == (long long)N * d && st[0] == (long long)H * N * d;
+}
+
+// Host-only checks of a descriptor, in the documented order; no HIP call.
+int validate(const fa_bwd_desc& a) {
+  if (!a.q || !a.k || !a.v || !a.out || !a.lse || !a.dout || !a.dq || !a.dk || !a.dv || !a.workspace)
+    return FA_ERR_NULL;
+  if (a.B < 1 || a.H < 1 || a.N < 1) return FA_ERR_SHAPE;
+  if ((long long)a.B * a.H * a.N >= (1LL << 31)) return FA_ERR_SHAPE;
+  if (a.d != 64 && a.d != 128) return FA_ERR_HEAD_DIM;
+  const long long* ts[8] = {a.q_stride,  a.k_stride,  a.v_stride,  a.o_stride,
+                            a.do_stride, a.dq_stride, a.dk_stride, a.dv_stride};
+  for (const long long* st : ts)
+    if (!strides_ok(st, a.N, a.d)) return FA_ERR_STRIDE;
+  for (int i = 0; i < 2; ++i)
+    if (a.lse_stride[i] < 0 || a.lse_stride[i] > (1LL << 40)) return FA_ERR_STRIDE;
   if (!std::isfinite(a.scale) || !(a.scale > 0.f)) return FA_ERR_SCALE;
   if (a.causal != 0 && a.causal != 1) return FA_ERR_ARG;
+  if (a.dtype != FA_DTYPE_BF16 && a.dtype != FA_DTYPE_F16) return FA_ERR_ARG;
   auto al = [](const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; };
   for (const void* t : {a.q, a.k, a.v, a.out, a.dout, (const void*)a.dq, (const void*)a.dk, (const void*)a.dv})
     if (!al(t, 16)) return FA_ERR_ALIGN;
   if (!al(a.lse, 4)) return FA_ERR_ALIGN;
   const long long need = workspace_bytes(a.B, a.H, a.N);
-  if (!al(a.ws, 256) || a.ws_bytes < need) return FA_ERR_WORKSPACE;
-  const size_t tb = (size_t)a.B * a.H * a.N * a.d * 2, lb = (size_t)a.B * a.H * a.N * 4;
-  const std::pair<const void*, size_t> written[4] = {{a.dq, tb}, {a.dk, tb}, {a.dv, tb}, {a.ws, (size_t)need}};
-  const std::pair<const void*, size_t> read[6] = {{a.q, tb}, {a.k, tb}, {a.v, tb}, {a.out, tb}, {a.dout, tb}, {a.lse, lb}};
+  if (!al(a.workspace, 256) || a.workspace_bytes < need) return FA_ERR_WORKSPACE;
+  auto fp = [&](const void* p, const long long st[3]) { return footprint(p, st, a.B, a.H, a.N, a.d); };
+  const long long lst[3] = {a.lse_stride[0], a.lse_stride[1], 1};
+  const Footprint written[4] = {fp(a.dq, a.dq_stride), fp(a.dk, a.dk_stride), fp(a.dv, a.dv_stride),
+                                {reinterpret_cast<uintptr_t>(a.workspace), need, 0, 0, 0}};
+  const Footprint read[6] = {fp(a.q, a.q_stride),      fp(a.k, a.k_stride),      fp(a.v, a.v_stride),
+                             fp(a.out, a.o_stride),    fp(a.dout, a.do_stride),
+                             {reinterpret_cast<uintptr_t>(a.lse), extent_bytes(lst, a.B, a.H, a.N, 1, 4), 0, 0, 0}};
   for (int i = 0; i < 4; ++i) {
     for (int j = i + 1; j < 4; ++j)
-      if (overlaps(written[i].first, written[i].second, written[j].first, written[j].second)) return FA_ERR_ALIAS;
+      if (may_overlap(written[i], written[j])) return FA_ERR_ALIAS;
     for (const auto& r : read)
-      if (overlaps(written[i].first, written[i].second, r.first, r.second)) return FA_ERR_ALIAS;
+      if (may_overlap(written[i], r)) return FA_ERR_ALIAS;
   }
   return FA_OK;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, typename E, bool STRIDED>
 hipError_t launch(const fa::BwdParams& p0, hipStream_t stream) {
   fa::BwdParams p = p0;
   const long long rows = (long long)p.BH * p.N;
   constexpr int kRowsPerBlock = 256 / (D / 8);
   const long long pre_blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL((fa::fa_bwd_pre_kernel<D>), dim3((unsigned)pre_blocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((fa::fa_bwd_pre_kernel<D, E, STRIDED>), dim3((unsigned)pre_blocks), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int kBK = kDkdvWaves<D> * 32;
   p.ntiles = (p.N + kBK - 1) / kBK;
-  hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<D, CAUSAL, kDkdvWaves<D>, kDkdvVlds<D>>),
+  hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<D, CAUSAL, kDkdvWaves<D>, kDkdvVlds<D>, E, STRIDED>),
                      dim3((unsigned)(p.BH * p.ntiles)), dim3(kDkdvWaves<D> * 64), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int kBQ = kDqWaves * 32;
   p.ntiles = (p.N + kBQ - 1) / kBQ;
-  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<D, CAUSAL, kDqWaves, kDqBK<D>>), dim3((unsigned)(p.BH * p.ntiles)),
-                     dim3(kDqWaves * 64), 0, stream, p);
+  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<D, CAUSAL, kDqWaves, kDqBK<D>, E, STRIDED>),
+                     dim3((unsigned)(p.BH * p.ntiles)), dim3(kDqWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 
-int run(const Args& a) {
+template <int D, bool CAUSAL>
+hipError_t launch_dt(const fa::BwdParams& p, int dtype, bool strided, hipStream_t s) {
+  if (dtype == FA_DTYPE_F16)
+    return strided ? launch<D, CAUSAL, fa::F16, true>(p, s) : launch<D, CAUSAL, fa::F16, false>(p, s);
+  return strided ? launch<D, CAUSAL, fa::Bf16, true>(p, s) : launch<D, CAUSAL, fa::Bf16, false>(p, s);
+}
+
+int run(const fa_bwd_desc& a) {
   const int st = validate(a);
   if (st != FA_OK) return st;
   const int dst = check_device();
@@ -134,18 +190,37 @@ int run(const Args& a) {
   p.dq = static_cast<uint16_t*>(a.dq);
   p.dk = static_cast<uint16_t*>(a.dk);
   p.dv = static_cast<uint16_t*>(a.dv);
-  p.lse2 = static_cast<float*>(a.ws);
+  p.lse2 = static_cast<float*>(a.workspace);
   p.dsum = p.lse2 + (long long)a.B * a.H * a.N;
-  p.BH = a.B * a.H, p.N = a.N;
+  p.q_sb = a.q_stride[0], p.q_sh = a.q_stride[1], p.q_rs = (int)a.q_stride[2];
+  p.k_sb = a.k_stride[0], p.k_sh = a.k_stride[1], p.k_rs = (int)a.k_stride[2];
+  p.v_sb = a.v_stride[0], p.v_sh = a.v_stride[1], p.v_rs = (int)a.v_stride[2];
+  p.o_sb = a.o_stride[0], p.o_sh = a.o_stride[1], p.o_rs = (int)a.o_stride[2];
+  p.do_sb = a.do_stride[0], p.do_sh = a.do_stride[1], p.do_rs = (int)a.do_stride[2];
+  p.dq_sb = a.dq_stride[0], p.dq_sh = a.dq_stride[1], p.dq_rs = (int)a.dq_stride[2];
+  p.dk_sb = a.dk_stride[0], p.dk_sh = a.dk_stride[1], p.dk_rs = (int)a.dk_stride[2];
+  p.dv_sb = a.dv_stride[0], p.dv_sh = a.dv_stride[1], p.dv_rs = (int)a.dv_stride[2];
+  p.l_sb = a.lse_stride[0], p.l_sh = a.lse_stride[1];
+  p.H = a.H, p.BH = a.B * a.H, p.N = a.N;
   p.qk_scale = (float)((double)a.scale * 1.4426950408889634);
   p.scale = a.scale;
+  // Every tensor contiguous [B, H, N, d] (lse [B, H, N]): the kernels that
+  // derive all addresses from (head, row).
+  bool strided = a.lse_stride[1] != a.N || a.lse_stride[0] != (long long)a.H * a.N;
+  const long long* ts[8] = {a.q_stride,  a.k_stride,  a.v_stride,  a.o_stride,
+                            a.do_stride, a.dq_stride, a.dk_stride, a.dv_stride};
+  for (const long long* t : ts) strided = strided || !contiguous(t, a.H, a.N, a.d);
   const hipStream_t s = static_cast<hipStream_t>(a.stream);
   hipError_t e;
   if (a.d == 64)
-    e = a.causal ? launch<64, true>(p, s) : launch<64, false>(p, s);
+    e = a.causal ? launch_dt<64, true>(p, a.dtype, strided, s) : launch_dt<64, false>(p, a.dtype, strided, s);
   else
-    e = a.causal ? launch<128, true>(p, s) : launch<128, false>(p, s);
+    e = a.causal ? launch_dt<128, true>(p, a.dtype, strided, s) : launch_dt<128, false>(p, a.dtype, strided, s);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+void set_contiguous(long long st[3], int H, int N, int d) {
+  st[0] = (long long)H * N * d, st[1] = (long long)N * d, st[2] = d;
 }
 
 }  // namespace
@@ -161,8 +236,28 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
            void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, void* workspace,
            long long ws_bytes, void* stream) {
   try {
-    const Args a{q, k, v, out, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, workspace, ws_bytes, stream};
+    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+    const int st = check_sizes(B, H, N, d);
+    if (st != FA_OK) return st;
+    fa_bwd_desc a{};
+    a.q = q, a.k = k, a.v = v, a.out = out, a.lse = lse, a.dout = dout, a.dq = dq, a.dk = dk, a.dv = dv;
+    a.B = B, a.H = H, a.N = N, a.d = d;
+    for (long long* t : {a.q_stride, a.k_stride, a.v_stride, a.o_stride, a.do_stride, a.dq_stride, a.dk_stride,
+                         a.dv_stride})
+      set_contiguous(t, H, N, d);
+    a.lse_stride[0] = (long long)H * N, a.lse_stride[1] = N;
+    a.scale = scale, a.causal = causal, a.dtype = FA_DTYPE_BF16;
+    a.workspace = workspace, a.workspace_bytes = ws_bytes, a.stream = stream;
     return run(a);
+  } catch (...) {
+    return FA_ERR_INTERNAL;
+  }
+}
+
+int fa_bwd_ex(const fa_bwd_desc* desc) {
+  try {
+    if (!desc) return FA_ERR_NULL;
+    return run(*desc);
   } catch (...) {
     return FA_ERR_INTERNAL;
   }

@@ -23,17 +23,18 @@
 // The split into a key-major and a query-major pass recomputes S and dP twice
 // (7 matrix products instead of 5) in exchange for no atomic traffic on dQ.
 //
-// MFMA mapping (v_mfma_f32_32x32x16_bf16; C lane l, register r holds row
+// Inputs and gradients are bf16 or fp16 (template E), contiguous or strided.
+// MFMA mapping (v_mfma_f32_32x32x16_{bf16,f16}; C lane l, register r holds row
 // 8(r/4) + 4(l/32) + r%4, column l%32):
 // * dK/dV pass: S = Q K^T and dP = dO V^T with Q (dO) rows read from LDS as the A
 //   operand and K (V) rows in VGPRs as the B operand, so a lane owns ONE key and
-//   16 queries; P and dS packed to bf16 are then already the B operand of
+//   16 queries; P and dS packed to 16 bits are then already the B operand of
 //   dV^T += dO^T P and dK^T += Q^T dS, whose A operands are dO and Q read
 //   transposed from LDS (ds_read_b64_tr_b16) in the order the C layout holds the
 //   queries.  Each lane needs LSE and D of its 16 queries: four 16-byte LDS
 //   reads each per 32 queries.
 // * dQ pass: S^T = K Q^T and dP^T = V dO^T (lane = one query, as in the
-//   forward), dS^T packed to bf16 is the B operand of dQ^T += K^T dS^T, with K
+//   forward), dS^T packed to 16 bits is the B operand of dQ^T += K^T dS^T, with K
 //   read transposed from LDS.
 // LDS tiles use the forward's XOR swizzle, which keeps both the row reads and
 // the transposed reads free of bank conflicts.
@@ -44,8 +45,10 @@ namespace fa {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
-// Kernel arguments of the backward.  All tensors contiguous [B, H, N, d]
-// (lse [B, H, N]); the workspace holds lse2 and dsum, [B, H, N] fp32 each.
+// Kernel arguments of the backward.  Tensors are addressed by element strides
+// (batch, head, row) with a contiguous head dimension; the STRIDED = false
+// kernels assume contiguous [B, H, N, d] (lse [B, H, N]) and ignore them.  The
+// workspace holds lse2 and dsum, contiguous [B*H, N] fp32 each.
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -58,9 +61,37 @@ struct BwdParams {
   uint16_t* dv;
   float* lse2;  // LSE * log2(e)
   float* dsum;  // D = rowsum(dO o O)
-  int BH, N, ntiles;
+  long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh, do_sb, do_sh;
+  long long dq_sb, dq_sh, dk_sb, dk_sh, dv_sb, dv_sh, l_sb, l_sh;
+  int q_rs, k_rs, v_rs, o_rs, do_rs, dq_rs, dk_rs, dv_rs;
+  int H, BH, N, ntiles;
   float qk_scale;  // scale * log2(e)
   float scale;
+};
+
+// Element offset of head bh of a tensor: strided, or contiguous [B, H, N, D].
+template <bool STRIDED, int D>
+__device__ __forceinline__ long long head_off(long long sb, long long sh, int bh, int H, int N) {
+  if constexpr (STRIDED) {
+    const int b = bh / H;
+    return b * sb + (bh - b * H) * sh;
+  } else {
+    return (long long)bh * N * D;
+  }
+}
+
+// Two packed 16-bit elements of type E, widened.
+template <typename E>
+struct Unpack2;
+template <>
+struct Unpack2<Bf16> {
+  static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+};
+template <>
+struct Unpack2<F16> {
+  static __device__ __forceinline__ float lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
+  static __device__ __forceinline__ float hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
 };
 
 // 4 bytes per lane, global -> LDS: lane l's word lands at dst + 4*l.
@@ -68,18 +99,16 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rsrc, char* dst, uin
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 4, voffset, 0, 0, 0);
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
 // A operand of 32x32x16 read transposed out of a row-major (swizzled) LDS
 // tile: rows (keys or queries) 16*step + {4g + 0..3, 8 + 4g + 0..3}, columns
 // db*32 + lane%32 -- the order in which a C fragment holds its rows.
-__device__ __forceinline__ bf16x8 read_tr(const char* base, int lo, int hi) {
+template <typename E>
+__device__ __forceinline__ typename E::v8 read_tr(const char* base, int lo, int hi) {
   const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + lo));
   const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + hi));
   const u32x4 w = {__builtin_bit_cast(u32x2, a)[0], __builtin_bit_cast(u32x2, a)[1], __builtin_bit_cast(u32x2, b)[0],
                    __builtin_bit_cast(u32x2, b)[1]};
-  return __builtin_bit_cast(bf16x8, w);
+  return __builtin_bit_cast(typename E::v8, w);
 }
 
 // Per-lane byte offsets of read_tr inside a tile: [db][0] for the low four
@@ -99,15 +128,16 @@ __device__ __forceinline__ void tr_offsets(int lane, int (&off)[D / 32][2]) {
     }
 }
 
-// A C fragment's 16 values as two bf16 B operands (16 rows each): element e of
-// operand h is register 8h + e.
-__device__ __forceinline__ void pack_b(const f32x16& x, bf16x8 (&b)[2]) {
+// A C fragment's 16 values as two 16-bit B operands (16 rows each): element e
+// of operand h is register 8h + e.
+template <typename E>
+__device__ __forceinline__ void pack_b(const f32x16& x, typename E::v8 (&b)[2]) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     u32x4 w;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[8 * h + 2 * e], x[8 * h + 2 * e + 1]);
-    b[h] = __builtin_bit_cast(bf16x8, w);
+    for (int e = 0; e < 4; ++e) w[e] = E::pack(x[8 * h + 2 * e], x[8 * h + 2 * e + 1]);
+    b[h] = __builtin_bit_cast(typename E::v8, w);
   }
 }
 
@@ -135,27 +165,34 @@ __device__ __forceinline__ void tile_of(int i, int total, int BH, int ntiles, bo
 }
 
 // ---- D = rowsum(dO o O) and LSE * log2(e), one row per D/8 lanes ------------
-template <int D>
+template <int D, typename E, bool STRIDED>
 __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const BwdParams pr) {
   constexpr int kLanes = D / 8;  // 16 bytes of a row per lane
   const long long rows = (long long)pr.BH * pr.N;
   const long long r = (long long)blockIdx.x * (256 / kLanes) + threadIdx.x / kLanes;
   const int c = (threadIdx.x % kLanes) * 8;
   float acc = 0.f;
+  int bh = 0, i = 0;
   if (r < rows) {
-    const u32x4 o = *reinterpret_cast<const u32x4*>(pr.out + r * D + c);
-    const u32x4 g = *reinterpret_cast<const u32x4*>(pr.dout + r * D + c);
+    bh = (int)(r / pr.N);
+    i = (int)(r - (long long)bh * pr.N);
+    const int o_rs = STRIDED ? pr.o_rs : D, do_rs = STRIDED ? pr.do_rs : D;
+    const uint16_t* orow = pr.out + head_off<STRIDED, D>(pr.o_sb, pr.o_sh, bh, pr.H, pr.N) + (long long)i * o_rs;
+    const uint16_t* grow = pr.dout + head_off<STRIDED, D>(pr.do_sb, pr.do_sh, bh, pr.H, pr.N) + (long long)i * do_rs;
+    const u32x4 o = *reinterpret_cast<const u32x4*>(orow + c);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(grow + c);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc = fmaf(bf16_lo(o[e]), bf16_lo(g[e]), acc);
-      acc = fmaf(bf16_hi(o[e]), bf16_hi(g[e]), acc);
+      acc = fmaf(Unpack2<E>::lo(o[e]), Unpack2<E>::lo(g[e]), acc);
+      acc = fmaf(Unpack2<E>::hi(o[e]), Unpack2<E>::hi(g[e]), acc);
     }
   }
 #pragma unroll
   for (int m = kLanes / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kLanes);
   if (r < rows && c == 0) {
     pr.dsum[r] = acc;
-    pr.lse2[r] = pr.lse[r] * kLog2e;
+    const long long l_off = STRIDED ? (long long)(bh / pr.H) * pr.l_sb + (bh % pr.H) * pr.l_sh : (long long)bh * pr.N;
+    pr.lse2[r] = pr.lse[l_off + i] * kLog2e;
   }
 }
 
@@ -164,8 +201,9 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const BwdParams pr) {
 // (d = 128): V rows stay in LDS for the whole sweep and are read as the B
 // operand of dP = dO V^T, which frees the 32 VGPRs that let two wavefronts share
 // a SIMD.
-template <int D, bool CAUSAL, int WAVES, bool VLDS>
+template <int D, bool CAUSAL, int WAVES, bool VLDS, typename E = Bf16, bool STRIDED = false>
 __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams pr) {
+  typedef typename E::v8 v8;
   constexpr int BQ = 64;                          // queries per staged tile
   constexpr int kBK = WAVES * 32;                 // keys per workgroup
   constexpr int kTileBytes = BQ * D * 2;          // one Q or dO tile
@@ -186,21 +224,27 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
 
   int bh, kt;
   tile_of((int)blockIdx.x, (int)gridDim.x, pr.BH, pr.ntiles, CAUSAL, bh, kt);
-  const long long hoff = (long long)bh * N * D;
-  const uint32_t tbytes = (uint32_t)N * D * 2;
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(pr.q + hoff, tbytes);
-  const __amdgpu_buffer_rsrc_t drs = make_rsrc(pr.dout + hoff, tbytes);
+  const int q_rs = STRIDED ? pr.q_rs : D, do_rs = STRIDED ? pr.do_rs : D;
+  const int k_rs = STRIDED ? pr.k_rs : D, v_rs = STRIDED ? pr.v_rs : D;
+  const __amdgpu_buffer_rsrc_t qrs =
+      make_rsrc(pr.q + head_off<STRIDED, D>(pr.q_sb, pr.q_sh, bh, pr.H, N), (uint32_t)((N - 1) * q_rs + D) * 2);
+  const __amdgpu_buffer_rsrc_t drs =
+      make_rsrc(pr.dout + head_off<STRIDED, D>(pr.do_sb, pr.do_sh, bh, pr.H, N), (uint32_t)((N - 1) * do_rs + D) * 2);
   const __amdgpu_buffer_rsrc_t lrs = make_rsrc(pr.lse2 + (long long)bh * N, (uint32_t)N * 4);
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(pr.dsum + (long long)bh * N, (uint32_t)N * 4);
   const int k0 = kt * kBK;
   const int kw = k0 + wave * 32;  // first key of this wavefront
 
-  uint32_t dma[kBlocksPerWave];
+  // Byte offsets of this lane's 16-byte pieces of a Q / dO tile (rows of the
+  // tile are swizzled 16-byte chunks in LDS).
+  uint32_t dma_q[kBlocksPerWave], dma_d[kBlocksPerWave];
 #pragma unroll
   for (int n = 0; n < kBlocksPerWave; ++n) {
     const int p = (wave + WAVES * n) * 64 + lane;
     const int row = p / (D / 8), pos = p % (D / 8);
-    dma[n] = row * D * 2 + ((pos ^ swz<D>(row)) << 4);
+    const int col = (pos ^ swz<D>(row)) << 4;
+    dma_q[n] = row * q_rs * 2 + col;
+    dma_d[n] = row * do_rs * 2 + col;
   }
   int roff[D / 16];  // row reads: row lr, chunk 2*ks + g
 #pragma unroll
@@ -209,27 +253,31 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
   tr_offsets<D>(lane, toff);
 
   // ---- this wavefront's K rows (and V rows, or the workgroup's V -> LDS) -------
-  bf16x8 kreg[D / 16], vreg[VLDS ? 1 : D / 16];
+  v8 kreg[D / 16], vreg[VLDS ? 1 : D / 16];
   {
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(pr.k + hoff, tbytes);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(pr.v + hoff, tbytes);
+    const __amdgpu_buffer_rsrc_t krs =
+        make_rsrc(pr.k + head_off<STRIDED, D>(pr.k_sb, pr.k_sh, bh, pr.H, N), (uint32_t)((N - 1) * k_rs + D) * 2);
+    const __amdgpu_buffer_rsrc_t vrs =
+        make_rsrc(pr.v + head_off<STRIDED, D>(pr.v_sb, pr.v_sh, bh, pr.H, N), (uint32_t)((N - 1) * v_rs + D) * 2);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const uint32_t off = ((kw + lr) * D + ks * 16 + g * 8) * 2;
-      kreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
-      if constexpr (!VLDS)
-        vreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
+      const uint32_t koff = ((kw + lr) * k_rs + ks * 16 + g * 8) * 2;
+      kreg[ks] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(krs, koff, 0, 0));
+      if constexpr (!VLDS) {
+        const uint32_t voff = ((kw + lr) * v_rs + ks * 16 + g * 8) * 2;
+        vreg[ks] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, 0, 0));
+      }
     }
     if constexpr (VLDS) {
       // kBK rows of V, swizzled like a tile; rows >= N read 0.  Waited for with
       // the first Q / dO tile.
       constexpr int kVBlocksPerWave = kVBytes / 1024 / WAVES;
-      const uint32_t gv = (uint32_t)k0 * D * 2;
+      const uint32_t gv = (uint32_t)k0 * v_rs * 2;
 #pragma unroll
       for (int n = 0; n < kVBlocksPerWave; ++n) {
         const int p = (wave + WAVES * n) * 64 + lane;
         const int row = p / (D / 8), pos = p % (D / 8);
-        dma16(vrs, vlds + (wave + WAVES * n) * 1024, gv + row * D * 2 + ((pos ^ swz<D>(row)) << 4));
+        dma16(vrs, vlds + (wave + WAVES * n) * 1024, gv + row * v_rs * 2 + ((pos ^ swz<D>(row)) << 4));
       }
     }
   }
@@ -246,13 +294,13 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
   auto issue_tile = [&](int j, int stage) {
     const int qs = qbeg + j * BQ;
     char* st = stage ? lds1 : lds0;
-    const uint32_t gq = (uint32_t)qs * D * 2;
+    const uint32_t gq = (uint32_t)qs * q_rs * 2, gd = (uint32_t)qs * do_rs * 2;
 #pragma unroll
     for (int n = 0; n < kBlocksPerWave; ++n) {
       const int b = wave + WAVES * n;
       if (kBlocks % WAVES == 0 || b < kBlocks) {
-        dma16(qrs, st + b * 1024, dma[n] + gq);
-        dma16(drs, st + kTileBytes + b * 1024, dma[n] + gq);
+        dma16(qrs, st + b * 1024, dma_q[n] + gq);
+        dma16(drs, st + kTileBytes + b * 1024, dma_d[n] + gd);
       }
     }
     if (wave == 0) dma4(lrs, st + 2 * kTileBytes, (uint32_t)(qs + lane) * 4);
@@ -275,18 +323,18 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(qst + qb * 32 * (D * 2) + roff[ks]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[ks], s, 0, 0, 0);
+        const v8 a = *reinterpret_cast<const v8*>(qst + qb * 32 * (D * 2) + roff[ks]);
+        s = E::mfma(a, kreg[ks], s);
       }
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(dst + qb * 32 * (D * 2) + roff[ks]);
-        bf16x8 b;
+        const v8 a = *reinterpret_cast<const v8*>(dst + qb * 32 * (D * 2) + roff[ks]);
+        v8 b;
         if constexpr (VLDS)
-          b = *reinterpret_cast<const bf16x8*>(vrow + roff[ks]);
+          b = *reinterpret_cast<const v8*>(vrow + roff[ks]);
         else
           b = vreg[ks];
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, dp, 0, 0, 0);
+        dp = E::mfma(a, b, dp);
       }
       // ---- P and dS -----------------------------------------------------------
 #pragma unroll
@@ -302,19 +350,17 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
           dp[r] = p * (dp[r] - Dq[e]);
         }
       }
-      bf16x8 pb[2], db16[2];
-      pack_b(s, pb);
-      pack_b(dp, db16);
+      v8 pb[2], db16[2];
+      pack_b<E>(s, pb);
+      pack_b<E>(dp, db16);
       // ---- dV^T += dO^T P, dK^T += Q^T dS --------------------------------------
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int rowoff = (2 * qb + h) * 16 * (D * 2);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(dst + rowoff, toff[db][0], toff[db][1]), pb[h],
-                                                           dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(qst + rowoff, toff[db][0], toff[db][1]), db16[h],
-                                                           dk[db], 0, 0, 0);
+          dv[db] = E::mfma(read_tr<E>(dst + rowoff, toff[db][0], toff[db][1]), pb[h], dv[db]);
+          dk[db] = E::mfma(read_tr<E>(qst + rowoff, toff[db][0], toff[db][1]), db16[h], dk[db]);
         }
       }
       // At 256 VGPRs (d = 128) two query blocks in flight do not fit: keep the
@@ -340,21 +386,22 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
   }
   if (j < ntiles) step(j, 0);
 
-  // ---- epilogue: dK = scale * (dK^T)^T, dV -> bf16 --------------------------------
+  // ---- epilogue: dK = scale * (dK^T)^T, dV -> E --------------------------------
   const int key = kw + lr;
   if (key < N) {
-    uint16_t* krow = pr.dk + hoff + (long long)key * D;
-    uint16_t* vout = pr.dv + hoff + (long long)key * D;
+    const int dk_rs = STRIDED ? pr.dk_rs : D, dv_rs = STRIDED ? pr.dv_rs : D;
+    uint16_t* krow = pr.dk + head_off<STRIDED, D>(pr.dk_sb, pr.dk_sh, bh, pr.H, N) + (long long)key * dk_rs;
+    uint16_t* vout = pr.dv + head_off<STRIDED, D>(pr.dv_sb, pr.dv_sh, bh, pr.H, N) + (long long)key * dv_rs;
     const float sc = pr.scale;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         u32x2 a, b;
-        a[0] = pack_bf16x2(dk[db][4 * rr + 0] * sc, dk[db][4 * rr + 1] * sc);
-        a[1] = pack_bf16x2(dk[db][4 * rr + 2] * sc, dk[db][4 * rr + 3] * sc);
-        b[0] = pack_bf16x2(dv[db][4 * rr + 0], dv[db][4 * rr + 1]);
-        b[1] = pack_bf16x2(dv[db][4 * rr + 2], dv[db][4 * rr + 3]);
+        a[0] = E::pack(dk[db][4 * rr + 0] * sc, dk[db][4 * rr + 1] * sc);
+        a[1] = E::pack(dk[db][4 * rr + 2] * sc, dk[db][4 * rr + 3] * sc);
+        b[0] = E::pack(dv[db][4 * rr + 0], dv[db][4 * rr + 1]);
+        b[1] = E::pack(dv[db][4 * rr + 2], dv[db][4 * rr + 3]);
         *reinterpret_cast<u32x2*>(krow + db * 32 + 8 * rr + 4 * g) = a;
         *reinterpret_cast<u32x2*>(vout + db * 32 + 8 * rr + 4 * g) = b;
       }
@@ -362,8 +409,9 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
 }
 
 // ---- dQ: one workgroup per WAVES*32 queries, key tiles of BK -----------------
-template <int D, bool CAUSAL, int WAVES, int BK>
+template <int D, bool CAUSAL, int WAVES, int BK, typename E = Bf16, bool STRIDED = false>
 __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams pr) {
+  typedef typename E::v8 v8;
   constexpr int kBQ = WAVES * 32;
   constexpr int kTileBytes = BK * D * 2;  // one K or V tile
   constexpr int kBlocks = kTileBytes / 1024;
@@ -382,24 +430,29 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams p
   int bh, rank;
   tile_of((int)blockIdx.x, (int)gridDim.x, pr.BH, nqt, CAUSAL, bh, rank);
   const int qt = CAUSAL ? nqt - 1 - rank : rank;  // causal: longest (last) query tile first
-  const long long hoff = (long long)bh * N * D;
-  const uint32_t tbytes = (uint32_t)N * D * 2;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(pr.k + hoff, tbytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(pr.v + hoff, tbytes);
+  const int q_rs = STRIDED ? pr.q_rs : D, do_rs = STRIDED ? pr.do_rs : D;
+  const int k_rs = STRIDED ? pr.k_rs : D, v_rs = STRIDED ? pr.v_rs : D;
+  const __amdgpu_buffer_rsrc_t krs =
+      make_rsrc(pr.k + head_off<STRIDED, D>(pr.k_sb, pr.k_sh, bh, pr.H, N), (uint32_t)((N - 1) * k_rs + D) * 2);
+  const __amdgpu_buffer_rsrc_t vrs =
+      make_rsrc(pr.v + head_off<STRIDED, D>(pr.v_sb, pr.v_sh, bh, pr.H, N), (uint32_t)((N - 1) * v_rs + D) * 2);
   const int q0 = qt * kBQ;
   const int qw = q0 + wave * 32;
   const int query = qw + lr;
 
   // ---- Q and dO rows -> VGPRs (B operands), LSE and D of this lane's query ----
-  bf16x8 qreg[D / 16], doreg[D / 16];
+  v8 qreg[D / 16], doreg[D / 16];
   {
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(pr.q + hoff, tbytes);
-    const __amdgpu_buffer_rsrc_t drs = make_rsrc(pr.dout + hoff, tbytes);
+    const __amdgpu_buffer_rsrc_t qrs =
+        make_rsrc(pr.q + head_off<STRIDED, D>(pr.q_sb, pr.q_sh, bh, pr.H, N), (uint32_t)((N - 1) * q_rs + D) * 2);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(pr.dout + head_off<STRIDED, D>(pr.do_sb, pr.do_sh, bh, pr.H, N),
+                                                 (uint32_t)((N - 1) * do_rs + D) * 2);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const uint32_t off = (query * D + ks * 16 + g * 8) * 2;
-      qreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
-      doreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(drs, off, 0, 0));
+      const uint32_t qoff = (query * q_rs + ks * 16 + g * 8) * 2;
+      const uint32_t doff = (query * do_rs + ks * 16 + g * 8) * 2;
+      qreg[ks] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff, 0, 0));
+      doreg[ks] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(drs, doff, 0, 0));
     }
   }
   float l2 = 0.f, dd = 0.f;
@@ -408,12 +461,14 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams p
     dd = pr.dsum[(long long)bh * N + query];
   }
 
-  uint32_t dma[kBlocksPerWave];
+  uint32_t dma_k[kBlocksPerWave], dma_v[kBlocksPerWave];
 #pragma unroll
   for (int n = 0; n < kBlocksPerWave; ++n) {
     const int p = (wave + WAVES * n) * 64 + lane;
     const int row = p / (D / 8), pos = p % (D / 8);
-    dma[n] = row * D * 2 + ((pos ^ swz<D>(row)) << 4);
+    const int col = (pos ^ swz<D>(row)) << 4;
+    dma_k[n] = row * k_rs * 2 + col;
+    dma_v[n] = row * v_rs * 2 + col;
   }
   int roff[D / 16];
 #pragma unroll
@@ -429,34 +484,34 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams p
   const int ntiles = (kend + BK - 1) / BK;
 
   auto issue_tile = [&](int j, int stage) {
-    const uint32_t gk = (uint32_t)(j * BK) * D * 2;
+    const uint32_t gk = (uint32_t)(j * BK) * k_rs * 2, gv = (uint32_t)(j * BK) * v_rs * 2;
     char* st = stage ? lds1 : lds0;
 #pragma unroll
     for (int n = 0; n < kBlocksPerWave; ++n) {
       const int b = wave + WAVES * n;
       if (kBlocks % WAVES == 0 || b < kBlocks) {
-        dma16(krs, st + b * 1024, dma[n] + gk);
-        dma16(vrs, st + kTileBytes + b * 1024, dma[n] + gk);
+        dma16(krs, st + b * 1024, dma_k[n] + gk);
+        dma16(vrs, st + kTileBytes + b * 1024, dma_v[n] + gv);
       }
     }
   };
 
   auto compute_tile = [&](const char* kst, int k0, bool masked) {
     const char* vst = kst + kTileBytes;
-    bf16x8 dsb[BK / 16];
+    v8 dsb[BK / 16];
 #pragma unroll
     for (int kb = 0; kb < BK / 32; ++kb) {
       // ---- S^T = K Q^T, dP^T = V dO^T (lane = query, 16 keys) ------------------
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kst + kb * 32 * (D * 2) + roff[ks]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s, 0, 0, 0);
+        const v8 a = *reinterpret_cast<const v8*>(kst + kb * 32 * (D * 2) + roff[ks]);
+        s = E::mfma(a, qreg[ks], s);
       }
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vst + kb * 32 * (D * 2) + roff[ks]);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, doreg[ks], dp, 0, 0, 0);
+        const v8 a = *reinterpret_cast<const v8*>(vst + kb * 32 * (D * 2) + roff[ks]);
+        dp = E::mfma(a, doreg[ks], dp);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -467,8 +522,8 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams p
         }
         dp[r] = p * (dp[r] - dd);
       }
-      bf16x8 b2[2];
-      pack_b(dp, b2);
+      v8 b2[2];
+      pack_b<E>(dp, b2);
       dsb[2 * kb] = b2[0];
       dsb[2 * kb + 1] = b2[1];
     }
@@ -477,8 +532,7 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams p
     for (int kk = 0; kk < BK / 16; ++kk)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(kst + kk * 16 * (D * 2), toff[db][0], toff[db][1]),
-                                                         dsb[kk], dq[db], 0, 0, 0);
+        dq[db] = E::mfma(read_tr<E>(kst + kk * 16 * (D * 2), toff[db][0], toff[db][1]), dsb[kk], dq[db]);
   };
 
   auto step = [&](int j, int stage) {
@@ -502,15 +556,16 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams p
   if (j < ntiles) step(j, 0);
 
   if (query < N) {
-    uint16_t* row = pr.dq + hoff + (long long)query * D;
+    const int dq_rs = STRIDED ? pr.dq_rs : D;
+    uint16_t* row = pr.dq + head_off<STRIDED, D>(pr.dq_sb, pr.dq_sh, bh, pr.H, N) + (long long)query * dq_rs;
     const float sc = pr.scale;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         u32x2 w;
-        w[0] = pack_bf16x2(dq[db][4 * rr + 0] * sc, dq[db][4 * rr + 1] * sc);
-        w[1] = pack_bf16x2(dq[db][4 * rr + 2] * sc, dq[db][4 * rr + 3] * sc);
+        w[0] = E::pack(dq[db][4 * rr + 0] * sc, dq[db][4 * rr + 1] * sc);
+        w[1] = E::pack(dq[db][4 * rr + 2] * sc, dq[db][4 * rr + 3] * sc);
         *reinterpret_cast<u32x2*>(row + db * 32 + 8 * rr + 4 * g) = w;
       }
   }

@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kVersion = 310;  // 0.3.1
+constexpr int kVersion = 400;  // 0.4.0
 
 using Launcher = hipError_t (*)(const fa::Params&, int B, hipStream_t);
 

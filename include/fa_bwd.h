@@ -61,6 +61,53 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
            void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, void* workspace,
            long long workspace_bytes, void* stream);
 
+/*
+ * General layouts and fp16: the operation of fa_bwd on tensors addressed by
+ * element strides (the head dimension contiguous), in bfloat16 or IEEE fp16.
+ * Heads stay square (every tensor has N rows per head); the mask and the
+ * formulas are those of fa_bwd.
+ *
+ *   q, k, v, out, dout   read only; element (b, h, i, c) of q at
+ *                        q[b*q_stride[0] + h*q_stride[1] + i*q_stride[2] + c],
+ *                        and likewise for each tensor with its own strides.
+ *                        A [B, N, H, d] tensor has strides {N*H*d, d, H*d}.
+ *   lse                  fp32, element (b, h, i) at
+ *                        lse[b*lse_stride[0] + h*lse_stride[1] + i].  Read only.
+ *   dq, dk, dv           written, every element, with their own strides.
+ *   dtype                FA_DTYPE_BF16 (0) or FA_DTYPE_F16 for all nine 16-bit
+ *                        tensors alike (else FA_ERR_ARG); products accumulate in
+ *                        fp32 and P, dS enter the matrix instruction in dtype.
+ *                        fp16 inputs must be finite.
+ *   workspace            as for fa_bwd (fa_bwd_workspace_bytes(B, H, N, d)).
+ * Stride rules (else FA_ERR_STRIDE): those of fa_fwd_desc for 16-bit
+ * elements: every stride >= 0 and a multiple of 8 elements, every row stride
+ * >= d, (N + 256) * row stride < 2^30; lse strides >= 0.
+ * Errors, in this order: FA_ERR_NULL (desc or a pointer), FA_ERR_SHAPE (B, H,
+ * N < 1, or B*H*N >= 2^31), FA_ERR_HEAD_DIM, FA_ERR_STRIDE, FA_ERR_SCALE,
+ * FA_ERR_ARG (causal, dtype), FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_ALIAS
+ * (judged on each tensor's whole byte extent, as for fa_bwd), FA_ERR_NO_DEVICE,
+ * FA_ERR_LAUNCH.  When every tensor is contiguous [B, H, N, d] (lse [B, H, N])
+ * the call runs the same kernels as fa_bwd, with identical results for bf16.
+ */
+typedef struct fa_bwd_desc {
+  const void *q, *k, *v, *out;
+  const float *lse;
+  const void *dout;
+  void *dq, *dk, *dv;
+  int B, H, N, d;
+  long long q_stride[3], k_stride[3], v_stride[3], o_stride[3], do_stride[3];
+  long long dq_stride[3], dk_stride[3], dv_stride[3];
+  long long lse_stride[2];
+  float scale;
+  int causal;
+  int dtype;
+  void *workspace;
+  long long workspace_bytes;
+  void *stream;
+} fa_bwd_desc;
+
+int fa_bwd_ex(const fa_bwd_desc *desc);
+
 #ifdef __cplusplus
 }
 #endif

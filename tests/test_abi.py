@@ -285,3 +285,94 @@ def test_bwd_valid_call_reaches_the_device_check(lib):
         pytest.skip("a GPU is present")
     assert bwd_call() == 8
     assert bwd_call(q=FAKE, k=FAKE, v=FAKE, nbytes=8 * 2 * 64) == 8  # inputs may alias; exact workspace size
+
+
+# ------------------------------------------------- backward, descriptor form
+
+def bwd_desc(**kw):
+    """A valid contiguous bf16 backward descriptor on fake pointers, then overrides
+    (stride fields take 3-tuples)."""
+    B, H, N, d = kw.pop("B", 1), kw.pop("H", 2), kw.pop("N", 64), kw.pop("d", 64)
+    a = fa.BwdDesc()
+    a.q, a.k, a.v, a.out, a.lse, a.dout = FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 5 * FAKE, 6 * FAKE
+    a.dq, a.dk, a.dv = 7 * FAKE, 8 * FAKE, 9 * FAKE
+    a.B, a.H, a.N, a.d = B, H, N, d
+    for name in ("q", "k", "v", "o", "do", "dq", "dk", "dv"):
+        setattr(a, name + "_stride", (ctypes.c_longlong * 3)(H * N * d, N * d, d))
+    a.lse_stride = (ctypes.c_longlong * 2)(H * N, N)
+    a.scale, a.causal, a.dtype = 0.125, 0, 0
+    a.workspace, a.workspace_bytes, a.stream = WS, 1 << 30, None
+    for key, val in kw.items():
+        if key.endswith("_stride"):
+            val = (ctypes.c_longlong * len(val))(*val)
+        setattr(a, key, val)
+    return a
+
+
+def bwd_ex(lib, **kw):
+    a = bwd_desc(**kw)
+    return lib.fa_bwd_ex(ctypes.byref(a))
+
+
+def packed(base, B, N, H, d, slot, slots=3):
+    """Pointer and strides of slot `slot` of a [B, N, slots, H, d] 16-bit buffer."""
+    return base + slot * H * d * 2, (N * slots * H * d, d, slots * H * d)
+
+
+def test_bwd_ex_null_descriptor(lib):
+    assert lib.fa_bwd_ex(None) == 1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dq=0), 1), (dict(workspace=0), 1),
+    (dict(N=0), 2), (dict(B=1 << 12, H=1 << 10, N=1 << 9), 2), (dict(d=256), 3), (dict(d=32), 3),
+    (dict(q_stride=(8192, 4096, 68)), 11),          # row stride not a multiple of 8 elements
+    (dict(dv_stride=(8192, 4096, 56)), 11),         # row stride < d
+    (dict(k_stride=(-8192, 4096, 64)), 11),
+    (dict(do_stride=(8192, 4096, 1 << 22)), 11),    # (N + 256) * row stride >= 2^30
+    (dict(lse_stride=(-1, 64)), 11),
+    (dict(scale=-1.0), 4), (dict(causal=3), 5), (dict(dtype=2), 5), (dict(dtype=7), 5),
+    (dict(out=4 * FAKE + 8), 6), (dict(lse=5 * FAKE + 2), 6),
+    (dict(workspace=WS + 128), 12), (dict(workspace_bytes=8 * 2 * 64 - 1), 12),
+    (dict(dk=7 * FAKE), 7),                         # dk is dq
+    (dict(dq=6 * FAKE + 4096), 7),                  # dq inside dout
+    (dict(workspace=9 * FAKE), 7),                  # the workspace overlaps dv
+])
+def test_bwd_ex_argument_errors(lib, kw, code):
+    assert bwd_ex(lib, **kw) == code
+
+
+def test_bwd_ex_interleaved_alias_rule(lib):
+    """dq, dk, dv interleaved in one packed [B, N, 3, H, d] buffer are disjoint
+    although their extents overlap; shifting one of them by 8 elements makes two
+    of them share bytes, and that is rejected."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    B, N, H, d = 2, 64, 2, 64
+    P = 16 * FAKE
+    g = [packed(P, B, N, H, d, s) for s in range(3)]
+    ok = dict(B=B, N=N, H=H, d=d, dq=g[0][0], dq_stride=g[0][1], dk=g[1][0], dk_stride=g[1][1], dv=g[2][0],
+              dv_stride=g[2][1], workspace_bytes=8 * B * H * N)
+    assert bwd_ex(lib, **ok) == 8  # valid: reaches the device check
+    bad = dict(ok, dk=g[1][0] - 16)
+    assert bwd_ex(lib, **bad) == 7
+    # q, k, v read from a packed buffer, dq beside them in the same rows: a
+    # [B, N, 4, H, d] buffer whose slot 3 is written.
+    Q = 32 * FAKE
+    r = [packed(Q, B, N, H, d, s, slots=4) for s in range(4)]
+    mixed = dict(ok, q=r[0][0], q_stride=r[0][1], k=r[1][0], k_stride=r[1][1], v=r[2][0], v_stride=r[2][1],
+                 dq=r[3][0], dq_stride=r[3][1])
+    assert bwd_ex(lib, **mixed) == 8
+    assert bwd_ex(lib, **dict(mixed, dq=r[2][0], dq_stride=r[2][1])) == 7  # dq would overwrite v
+
+
+def test_bwd_ex_valid_layouts_reach_the_device_check(lib):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    B, N, H, d = 1, 64, 2, 128
+    bnhd = (N * H * d, d, H * d)
+    assert bwd_ex(lib, B=B, N=N, H=H, d=d, q_stride=bnhd, k_stride=bnhd, v_stride=bnhd, o_stride=bnhd,
+                  do_stride=bnhd, dq_stride=bnhd, dk_stride=bnhd, dv_stride=bnhd, lse_stride=(2 * N * H, 2 * N),
+                  dtype=1) == 8
