@@ -128,6 +128,25 @@ __device__ __forceinline__ void tr_offsets(int lane, int (&off)[D / 32][2]) {
     }
 }
 
+// Direct loads of a tile in 1 KB blocks: block b covers rows kRows * b ..
+// kRows * (b + 1) - 1 (kRows = 512 / D) and lane l fills row kRows * b + l /
+// (D / 8), LDS position l % (D / 8), fetching the global chunk that the
+// swizzle puts there.  The swizzle depends on row bits 0..3 only, so when
+// kRows * WAVES is a multiple of 16 the blocks b = wave + WAVES * n of one
+// wave share a per-lane byte offset; block n then adds rows kRows * b.
+template <int D, int WAVES>
+struct BlockDma {
+  static constexpr int kRows = 512 / D;
+  static_assert((kRows * WAVES) % 16 == 0, "one lane offset per wave needs the swizzle's 16-row period");
+  // Per-lane part of the byte offset, for a tensor with row stride rs.
+  static __device__ __forceinline__ uint32_t lane_off(int lane, int wave, int rs) {
+    const int row_l = lane / (D / 8), pos = lane % (D / 8);
+    return row_l * rs * 2 + ((pos ^ swz<D>(kRows * wave + row_l)) << 4);
+  }
+  // First row of block n of this wave.
+  static __device__ __forceinline__ int row0(int wave, int n) { return kRows * (wave + WAVES * n); }
+};
+
 // A C fragment's 16 values as two 16-bit B operands (16 rows each): element e
 // of operand h is register 8h + e.
 template <typename E>
@@ -219,7 +238,8 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
 
   const int N = pr.N;
   const float qk_scale = pr.qk_scale;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, lr = lane & 31;
 
   int bh, kt;
@@ -235,17 +255,8 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
   const int k0 = kt * kBK;
   const int kw = k0 + wave * 32;  // first key of this wavefront
 
-  // Byte offsets of this lane's 16-byte pieces of a Q / dO tile (rows of the
-  // tile are swizzled 16-byte chunks in LDS).
-  uint32_t dma_q[kBlocksPerWave], dma_d[kBlocksPerWave];
-#pragma unroll
-  for (int n = 0; n < kBlocksPerWave; ++n) {
-    const int p = (wave + WAVES * n) * 64 + lane;
-    const int row = p / (D / 8), pos = p % (D / 8);
-    const int col = (pos ^ swz<D>(row)) << 4;
-    dma_q[n] = row * q_rs * 2 + col;
-    dma_d[n] = row * do_rs * 2 + col;
-  }
+  using Dma = BlockDma<D, WAVES>;
+  const uint32_t dma_q = Dma::lane_off(lane, wave, q_rs), dma_d = Dma::lane_off(lane, wave, do_rs);
   int roff[D / 16];  // row reads: row lr, chunk 2*ks + g
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) roff[ks] = lds_offset<D>(lr, 2 * ks + g);
@@ -272,13 +283,11 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
       // kBK rows of V, swizzled like a tile; rows >= N read 0.  Waited for with
       // the first Q / dO tile.
       constexpr int kVBlocksPerWave = kVBytes / 1024 / WAVES;
-      const uint32_t gv = (uint32_t)k0 * v_rs * 2;
+      const uint32_t dma_v = Dma::lane_off(lane, wave, v_rs);
 #pragma unroll
-      for (int n = 0; n < kVBlocksPerWave; ++n) {
-        const int p = (wave + WAVES * n) * 64 + lane;
-        const int row = p / (D / 8), pos = p % (D / 8);
-        dma16(vrs, vlds + (wave + WAVES * n) * 1024, gv + row * v_rs * 2 + ((pos ^ swz<D>(row)) << 4));
-      }
+      for (int n = 0; n < kVBlocksPerWave; ++n)
+        dma16(vrs, vlds + ((CAUSAL && STRIDED) ? (tid >> 6) + WAVES * n : wave + WAVES * n) * 1024,
+              dma_v + (uint32_t)(k0 + Dma::row0(wave, n)) * v_rs * 2);
     }
   }
   const char* vrow = vlds + wave * 32 * (D * 2);  // this wavefront's V rows
@@ -299,8 +308,13 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
     for (int n = 0; n < kBlocksPerWave; ++n) {
       const int b = wave + WAVES * n;
       if (kBlocks % WAVES == 0 || b < kBlocks) {
-        dma16(qrs, st + b * 1024, dma_q[n] + gq);
-        dma16(drs, st + kTileBytes + b * 1024, dma_d[n] + gd);
+        const uint32_t r0 = (uint32_t)Dma::row0(wave, n);
+        // Block b's LDS slot.  The causal strided kernel takes it from the
+        // per-lane wave index: from the scalar one this compiler emits an
+        // LDS-aperture check it cannot encode (instruction selection error).
+        char* dst = st + ((CAUSAL && STRIDED) ? (tid >> 6) + WAVES * n : b) * 1024;
+        dma16(qrs, dst, dma_q + r0 * q_rs * 2 + gq);
+        dma16(drs, dst + kTileBytes, dma_d + r0 * do_rs * 2 + gd);
       }
     }
     if (wave == 0) dma4(lrs, st + 2 * kTileBytes, (uint32_t)(qs + lane) * 4);
@@ -424,7 +438,8 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams p
 
   const int N = pr.N, nqt = pr.ntiles;
   const float qk_scale = pr.qk_scale;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, lr = lane & 31;
 
   int bh, rank;
@@ -461,15 +476,8 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams p
     dd = pr.dsum[(long long)bh * N + query];
   }
 
-  uint32_t dma_k[kBlocksPerWave], dma_v[kBlocksPerWave];
-#pragma unroll
-  for (int n = 0; n < kBlocksPerWave; ++n) {
-    const int p = (wave + WAVES * n) * 64 + lane;
-    const int row = p / (D / 8), pos = p % (D / 8);
-    const int col = (pos ^ swz<D>(row)) << 4;
-    dma_k[n] = row * k_rs * 2 + col;
-    dma_v[n] = row * v_rs * 2 + col;
-  }
+  using Dma = BlockDma<D, WAVES>;
+  const uint32_t dma_k = Dma::lane_off(lane, wave, k_rs), dma_v = Dma::lane_off(lane, wave, v_rs);
   int roff[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) roff[ks] = lds_offset<D>(lr, 2 * ks + g);
@@ -490,8 +498,10 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams p
     for (int n = 0; n < kBlocksPerWave; ++n) {
       const int b = wave + WAVES * n;
       if (kBlocks % WAVES == 0 || b < kBlocks) {
-        dma16(krs, st + b * 1024, dma_k[n] + gk);
-        dma16(vrs, st + kTileBytes + b * 1024, dma_v[n] + gv);
+        const uint32_t r0 = (uint32_t)Dma::row0(wave, n);
+        char* dst = st + b * 1024;
+        dma16(krs, dst, dma_k + r0 * k_rs * 2 + gk);
+        dma16(vrs, dst + kTileBytes, dma_v + r0 * v_rs * 2 + gv);
       }
     }
   };
