@@ -69,6 +69,11 @@ def _load():
                 ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
             lib.oracle_attention_bwd_dt.restype = ctypes.c_int
             lib.oracle_attention_bwd_dt.argtypes = lib.oracle_attention_bwd.argtypes + [ctypes.c_int]
+            lib.oracle_attention_bwd_qk.restype = ctypes.c_int
+            lib.oracle_attention_bwd_qk.argtypes = [
+                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
             lib.oracle_num_threads.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -139,22 +144,27 @@ def attention_rows_f32(q, k, v, scale: float, causal: bool, rows=None):
 
 
 def attention_bwd(q, k, v, dout, scale: float, causal: bool, dtype: str = "bf16"):
-    """Gradients (dq, dk, dv) of sum(dout * out) in fp64, each [B, H, N, d].
+    """Gradients (dq, dk, dv) of sum(dout * out) in fp64.
 
-    ``q, k, v, dout``: uint16 bit arrays [B, H, N, d] (square heads) of bfloat16
-    or (``dtype="f16"``) fp16 values.  Follows ``oracle_attention_bwd_dt`` in
-    ``oracle.c``.
+    ``q, dout``: uint16 bit arrays [B, H, Nq, d]; ``k, v``: [B, H, Nk, d]; of
+    bfloat16 or (``dtype="f16"``) fp16 values.  Causal masking is top-left
+    (key j permitted to query i iff j <= i).  Returns dq [B, H, Nq, d] and dk,
+    dv [B, H, Nk, d].  Follows ``oracle_attention_bwd_qk`` in ``oracle.c``.
     """
-    arrs = [np.ascontiguousarray(a, dtype=np.uint16) for a in (q, k, v, dout)]
-    if arrs[0].ndim != 4 or any(a.shape != arrs[0].shape for a in arrs):
-        raise ValueError("q, k, v, dout must share one [B, H, N, d] shape")
-    B, H, N, d = arrs[0].shape
-    dq, dk, dv = (np.empty((B, H, N, d), dtype=np.float64) for _ in range(3))
-    rc = _load().oracle_attention_bwd_dt(*(a.ctypes.data for a in arrs), B, H, N, d, float(scale),
-                                         int(bool(causal)), dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
-                                         DTYPES[dtype])
+    q, k, v, dout = (np.ascontiguousarray(a, dtype=np.uint16) for a in (q, k, v, dout))
+    if q.ndim != 4 or dout.shape != q.shape or k.ndim != 4 or v.shape != k.shape:
+        raise ValueError("q, dout must share one [B, H, Nq, d] shape and k, v one [B, H, Nk, d] shape")
+    B, H, Nq, d = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
+        raise ValueError("q and k must agree on B, H and d")
+    Nk = k.shape[2]
+    dq = np.empty((B, H, Nq, d), dtype=np.float64)
+    dk, dv = (np.empty((B, H, Nk, d), dtype=np.float64) for _ in range(2))
+    rc = _load().oracle_attention_bwd_qk(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data, B, H, Nq,
+                                         Nk, d, float(scale), int(bool(causal)), dq.ctypes.data, dk.ctypes.data,
+                                         dv.ctypes.data, DTYPES[dtype])
     if rc != 0:
-        raise RuntimeError("oracle_attention_bwd failed with code %d" % rc)
+        raise RuntimeError("oracle_attention_bwd_qk failed with code %d" % rc)
     return dq, dk, dv
 
 

@@ -233,24 +233,27 @@ int oracle_attention_rows(const uint16_t *q, const uint16_t *k, const uint16_t *
  *   dS_ij = P_ij (dP_ij - D_i)
  *   dQ_i  = scale sum_j dS_ij k_j,    dK_j = scale sum_i dS_ij q_i
  *
- * Square heads, contiguous [B, H, N, d] inputs of bfloat16 (dtype 0) or fp16
- * (dtype 1); dq, dk, dv are
- * B*H*N*d doubles.  One score row at a time (no N x N buffer): the dQ row is
- * finished per query, dK and dV accumulate over queries; each head is one
- * OpenMP task, so accumulation order is fixed.  Returns 0, 1 on a bad argument,
- * 2 if scratch memory is exhausted.
+ * Nq query rows over Nk key rows: q, dout (and dq) contiguous [B, H, Nq, d],
+ * k, v (and dk, dv) contiguous [B, H, Nk, d], of bfloat16 (dtype 0) or fp16
+ * (dtype 1); dq, dk, dv are doubles.  The permitted keys are those of the
+ * forward oracle: all of them, or when causal j <= i (top-left alignment, so
+ * with Nq < Nk the keys j >= Nq are never permitted and their gradients are 0).
+ * One score row at a time (no Nq x Nk buffer): the dQ row is finished per
+ * query, dK and dV accumulate over queries; each head is one OpenMP task, so
+ * accumulation order is fixed.  Returns 0, 1 on a bad argument, 2 if scratch
+ * memory is exhausted.
  */
-int oracle_attention_bwd_dt(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
-                            int64_t B, int64_t H, int64_t N, int64_t d, double scale, int causal,
+int oracle_attention_bwd_qk(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                            int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, double scale, int causal,
                             double *dq, double *dk, double *dv, int dtype) {
   if (!q || !k || !v || !dout || !dq || !dk || !dv) return 1;
   if (dtype != 0 && dtype != 1) return 1;
-  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 1;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return 1;
   int failed = 0;
 #pragma omp parallel
   {
-    double *p = (double *)malloc((size_t)N * sizeof(double));
-    double *dp = (double *)malloc((size_t)N * sizeof(double));
+    double *p = (double *)malloc((size_t)Nk * sizeof(double));
+    double *dp = (double *)malloc((size_t)Nk * sizeof(double));
     double *qi = (double *)malloc((size_t)d * sizeof(double));
     double *gi = (double *)malloc((size_t)d * sizeof(double));
     if (!p || !dp || !qi || !gi) {
@@ -259,12 +262,12 @@ int oracle_attention_bwd_dt(const uint16_t *q, const uint16_t *k, const uint16_t
     } else {
 #pragma omp for schedule(dynamic, 1)
       for (int64_t head = 0; head < B * H; ++head) {
-        const uint16_t *qh = q + head * N * d, *kh = k + head * N * d;
-        const uint16_t *vh = v + head * N * d, *gh = dout + head * N * d;
-        double *dqh = dq + head * N * d, *dkh = dk + head * N * d, *dvh = dv + head * N * d;
-        for (int64_t x = 0; x < N * d; ++x) dkh[x] = dvh[x] = 0.0;
-        for (int64_t i = 0; i < N; ++i) {
-          const int64_t nkeys = causal ? i + 1 : N;
+        const uint16_t *qh = q + head * Nq * d, *kh = k + head * Nk * d;
+        const uint16_t *vh = v + head * Nk * d, *gh = dout + head * Nq * d;
+        double *dqh = dq + head * Nq * d, *dkh = dk + head * Nk * d, *dvh = dv + head * Nk * d;
+        for (int64_t x = 0; x < Nk * d; ++x) dkh[x] = dvh[x] = 0.0;
+        for (int64_t i = 0; i < Nq; ++i) {
+          const int64_t nkeys = (causal && i + 1 < Nk) ? i + 1 : Nk;
           for (int64_t c = 0; c < d; ++c) {
             qi[c] = oracle_to_f64(qh[i * d + c], dtype);
             gi[c] = oracle_to_f64(gh[i * d + c], dtype);
@@ -306,6 +309,13 @@ int oracle_attention_bwd_dt(const uint16_t *q, const uint16_t *k, const uint16_t
     free(gi);
   }
   return failed ? 2 : 0;
+}
+
+/* Square heads, N queries over N keys. */
+int oracle_attention_bwd_dt(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                            int64_t B, int64_t H, int64_t N, int64_t d, double scale, int causal,
+                            double *dq, double *dk, double *dv, int dtype) {
+  return oracle_attention_bwd_qk(q, k, v, dout, B, H, N, N, d, scale, causal, dq, dk, dv, dtype);
 }
 
 /* bfloat16 inputs. */

@@ -94,3 +94,62 @@ def test_f16_gradients_match_finite_differences(N, d, causal):
             args_m = {"q": (Xm, K, V), "k": (Q, Xm, V), "v": (Q, K, Xm)}[name]
             num[idx] = (f(*args_p) - f(*args_m)) / (2 * eps)
         assert np.allclose(grad[0, 0], num, atol=1e-7, rtol=1e-6), name
+
+
+@pytest.mark.parametrize("Nq,Nk,causal", [(3, 7, False), (3, 7, True), (8, 5, True), (6, 2, False)])
+def test_non_square_gradients_match_finite_differences(Nq, Nk, causal):
+    """Nq queries over Nk keys, causal top-left (j <= i): the oracle's gradients
+    match central differences of the independent NumPy forward (np.tril of an
+    Nq x Nk matrix keeps exactly j <= i)."""
+    d = 4
+    q, _, _ = random_qkv(1300 + Nq, 1, 1, Nq, d, sigma_qk=1.5)
+    _, k, v = random_qkv(1350 + Nk, 1, 1, Nk, d, sigma_qk=1.5)
+    g, _, _ = random_qkv(1400 + Nq + Nk, 1, 1, Nq, d)
+    scale = float(np.float32(0.5))
+    dq, dk, dv = oracle.attention_bwd(q, k, v, g, scale, causal)
+    assert dq.shape == (1, 1, Nq, d) and dk.shape == dv.shape == (1, 1, Nk, d)
+    Q, K, V, G = (bf16_bits_to_f64(a)[0, 0] for a in (q, k, v, g))
+
+    def f(Q_, K_, V_):
+        return float(np.sum(G * forward_np(Q_, K_, V_, scale, causal)))
+
+    eps = 1e-6
+    for name, X, grad in (("q", Q, dq), ("k", K, dk), ("v", V, dv)):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(*X.shape):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[idx] += eps
+            Xm[idx] -= eps
+            args_p = {"q": (Xp, K, V), "k": (Q, Xp, V), "v": (Q, K, Xp)}[name]
+            args_m = {"q": (Xm, K, V), "k": (Q, Xm, V), "v": (Q, K, Xm)}[name]
+            num[idx] = (f(*args_p) - f(*args_m)) / (2 * eps)
+        assert np.allclose(grad[0, 0], num, atol=1e-7, rtol=1e-6), name
+
+
+def test_non_square_causal_keys_beyond_the_queries_get_no_gradient():
+    """Causal top-left with Nq < Nk: keys j >= Nq are permitted to no query, so
+    their dK and dV are exactly 0; the value gradients still sum to the
+    upstream gradients' sum (each row's weights sum to 1)."""
+    q, _, _ = random_qkv(1500, 1, 2, 10, 8)
+    _, k, v = random_qkv(1501, 1, 2, 25, 8)
+    g, _, _ = random_qkv(1502, 1, 2, 10, 8)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, g, 0.3, True)
+    assert not np.any(dk[:, :, 10:]) and not np.any(dv[:, :, 10:])
+    assert np.any(dk[:, :, :10]) and np.any(dv[:, :, :10])
+    assert np.allclose(dv.sum(axis=2), bf16_bits_to_f64(g).sum(axis=2), atol=1e-12)
+    assert np.abs(dk.sum(axis=2)).max() < 1e-12
+
+
+def test_square_entry_points_agree():
+    """The square entry points are the Nq = Nk case of the general one."""
+    import ctypes
+    q, k, v = random_qkv(1600, 1, 2, 9, 4)
+    g, _, _ = random_qkv(1601, 1, 2, 9, 4)
+    a = oracle.attention_bwd(q, k, v, g, 0.4, True)
+    out = [np.empty((1, 2, 9, 4)) for _ in range(3)]
+    arrs = [np.ascontiguousarray(x) for x in (q, k, v, g)]
+    rc = oracle._load().oracle_attention_bwd(*(x.ctypes.data for x in arrs), 1, 2, 9, 4, ctypes.c_double(0.4), 1,
+                                             *(o.ctypes.data for o in out))
+    assert rc == 0
+    for x, y in zip(a, out):
+        assert np.array_equal(x, y)
