@@ -68,7 +68,7 @@ class BwdDesc(ctypes.Structure):
                 ("lse_stride", _LL2),
                 ("scale", ctypes.c_float), ("causal", ctypes.c_int), ("dtype", ctypes.c_int),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_longlong),
-                ("stream", ctypes.c_void_p)]
+                ("stream", ctypes.c_void_p), ("Nk", ctypes.c_int)]
 
 
 DTYPE_BF16, DTYPE_F16, DTYPE_F32 = 0, 1, 2
@@ -388,17 +388,21 @@ def fa_bwd_ex_ptr(desc: BwdDesc) -> int:
 
 def fa_bwd_ex(q, k, v, out, lse, dout, scale: float | None = None, causal: bool = False, dq=None, dk=None,
               dv=None, workspace=None, stream=None):
-    """Attention backward on strided bf16 or fp16 views (square heads).
+    """Attention backward on strided bf16 or fp16 views, Nq queries over Nk keys.
 
-    ``q, k, v, out, dout`` are [B, H, N, d] views of one dtype with a contiguous
-    last dimension (a [B, N, H, d] tensor is passed as ``t.transpose(1, 2)``),
-    ``lse`` a [B, H, N] fp32 view with unit row stride.  ``dq, dk, dv``
-    (default: new contiguous tensors) are [B, H, N, d] views of that dtype.
-    Returns ``(dq, dk, dv)``; enqueued on ``stream``, no synchronisation.
+    ``q, out, dout`` are [B, H, Nq, d] and ``k, v`` [B, H, Nk, d] views of one
+    dtype with a contiguous last dimension (a [B, N, H, d] tensor is passed as
+    ``t.transpose(1, 2)``), ``lse`` a [B, H, Nq] fp32 view with unit row stride:
+    ``fa_fwd_ex``'s outputs for the same scale and (top-left) mask.  ``dq``
+    (default: new) is shaped like q, ``dk, dv`` like k.  Returns
+    ``(dq, dk, dv)``; enqueued on ``stream``, no synchronisation.
     """
     import torch
-    if q.dim() != 4 or any(t.dim() != 4 or t.shape != q.shape for t in (k, v, out, dout)):
-        raise ValueError("q, k, v, out, dout must share one [B, H, N, d] shape")
+    if q.dim() != 4 or any(t.dim() != 4 or t.shape != q.shape for t in (out, dout)):
+        raise ValueError("q, out, dout must share one [B, H, Nq, d] shape")
+    if k.dim() != 4 or v.shape != k.shape or k.shape[0] != q.shape[0] or k.shape[1] != q.shape[1] \
+            or k.shape[3] != q.shape[3]:
+        raise ValueError("k, v must share one [B, H, Nk, d] shape agreeing with q on B, H, d")
     et = q.dtype
     if et not in (torch.bfloat16, torch.float16):
         raise ValueError("the backward takes bfloat16 or float16 tensors")
@@ -406,16 +410,17 @@ def fa_bwd_ex(q, k, v, out, lse, dout, scale: float | None = None, causal: bool 
         if t.dtype != et or not t.is_cuda or t.stride(3) != 1:
             raise ValueError("q, k, v, out, dout must be device views of one dtype with a contiguous last dimension")
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or lse.stride(2) != 1:
-        raise ValueError("lse must be an fp32 [B, H, N] view with unit row stride")
+        raise ValueError("lse must be an fp32 [B, H, Nq] view with unit row stride")
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
     grads = []
-    for g in (dq, dk, dv):
+    for g, shape in ((dq, (B, H, N, d)), (dk, (B, H, Nk, d)), (dv, (B, H, Nk, d))):
         if g is None:
-            g = torch.empty((B, H, N, d), dtype=et, device=q.device)
-        if g.shape != q.shape or g.dtype != et or g.stride(3) != 1:
-            raise ValueError("dq, dk, dv must be [B, H, N, d] views of q's dtype with a contiguous last dimension")
+            g = torch.empty(shape, dtype=et, device=q.device)
+        if tuple(g.shape) != shape or g.dtype != et or g.stride(3) != 1:
+            raise ValueError("dq must be shaped like q and dk, dv like k, in q's dtype with a contiguous last dimension")
         grads.append(g)
     need = bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
@@ -423,7 +428,7 @@ def fa_bwd_ex(q, k, v, out, lse, dout, scale: float | None = None, causal: bool 
     desc = BwdDesc()
     desc.q, desc.k, desc.v, desc.out, desc.lse, desc.dout = (t.data_ptr() for t in (q, k, v, out, lse, dout))
     desc.dq, desc.dk, desc.dv = (g.data_ptr() for g in grads)
-    desc.B, desc.H, desc.N, desc.d = B, H, N, d
+    desc.B, desc.H, desc.N, desc.d, desc.Nk = B, H, N, d, Nk
     for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", out), ("do_stride", dout),
                     ("dq_stride", grads[0]), ("dk_stride", grads[1]), ("dv_stride", grads[2])):
         setattr(desc, name, _LL3(*t.stride()[:3]))

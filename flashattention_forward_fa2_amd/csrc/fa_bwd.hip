@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -108,17 +109,22 @@ bool contiguous(const long long st[3], int H, int N, int d) {
   return st[2] == d && st[1] == (long long)N * d && st[0] == (long long)H * N * d;
 }
 
+// Key rows per head of a descriptor (0 selects the square case).
+int key_rows(const fa_bwd_desc& a) { return a.Nk == 0 ? a.N : a.Nk; }
+
 // Host-only checks of a descriptor, in the documented order; no HIP call.
 int validate(const fa_bwd_desc& a) {
   if (!a.q || !a.k || !a.v || !a.out || !a.lse || !a.dout || !a.dq || !a.dk || !a.dv || !a.workspace)
     return FA_ERR_NULL;
-  if (a.B < 1 || a.H < 1 || a.N < 1) return FA_ERR_SHAPE;
-  if ((long long)a.B * a.H * a.N >= (1LL << 31)) return FA_ERR_SHAPE;
+  const int Nk = key_rows(a);
+  if (a.B < 1 || a.H < 1 || a.N < 1 || Nk < 1) return FA_ERR_SHAPE;
+  if ((long long)a.B * a.H * std::max(a.N, Nk) >= (1LL << 31)) return FA_ERR_SHAPE;
   if (a.d != 64 && a.d != 128) return FA_ERR_HEAD_DIM;
-  const long long* ts[8] = {a.q_stride,  a.k_stride,  a.v_stride,  a.o_stride,
-                            a.do_stride, a.dq_stride, a.dk_stride, a.dv_stride};
-  for (const long long* st : ts)
-    if (!strides_ok(st, a.N, a.d)) return FA_ERR_STRIDE;
+  // q, out, dout, dq: N rows per head; k, v, dk, dv: Nk rows.
+  const long long* tq[4] = {a.q_stride, a.o_stride, a.do_stride, a.dq_stride};
+  const long long* tk[4] = {a.k_stride, a.v_stride, a.dk_stride, a.dv_stride};
+  for (int i = 0; i < 4; ++i)
+    if (!strides_ok(tq[i], a.N, a.d) || !strides_ok(tk[i], Nk, a.d)) return FA_ERR_STRIDE;
   for (int i = 0; i < 2; ++i)
     if (a.lse_stride[i] < 0 || a.lse_stride[i] > (1LL << 40)) return FA_ERR_STRIDE;
   if (!std::isfinite(a.scale) || !(a.scale > 0.f)) return FA_ERR_SCALE;
@@ -130,12 +136,13 @@ int validate(const fa_bwd_desc& a) {
   if (!al(a.lse, 4)) return FA_ERR_ALIGN;
   const long long need = workspace_bytes(a.B, a.H, a.N);
   if (!al(a.workspace, 256) || a.workspace_bytes < need) return FA_ERR_WORKSPACE;
-  auto fp = [&](const void* p, const long long st[3]) { return footprint(p, st, a.B, a.H, a.N, a.d); };
+  auto fq = [&](const void* p, const long long st[3]) { return footprint(p, st, a.B, a.H, a.N, a.d); };
+  auto fk = [&](const void* p, const long long st[3]) { return footprint(p, st, a.B, a.H, Nk, a.d); };
   const long long lst[3] = {a.lse_stride[0], a.lse_stride[1], 1};
-  const Footprint written[4] = {fp(a.dq, a.dq_stride), fp(a.dk, a.dk_stride), fp(a.dv, a.dv_stride),
+  const Footprint written[4] = {fq(a.dq, a.dq_stride), fk(a.dk, a.dk_stride), fk(a.dv, a.dv_stride),
                                 {reinterpret_cast<uintptr_t>(a.workspace), need, 0, 0, 0}};
-  const Footprint read[6] = {fp(a.q, a.q_stride),      fp(a.k, a.k_stride),      fp(a.v, a.v_stride),
-                             fp(a.out, a.o_stride),    fp(a.dout, a.do_stride),
+  const Footprint read[6] = {fq(a.q, a.q_stride),      fk(a.k, a.k_stride),      fk(a.v, a.v_stride),
+                             fq(a.out, a.o_stride),    fq(a.dout, a.do_stride),
                              {reinterpret_cast<uintptr_t>(a.lse), extent_bytes(lst, a.B, a.H, a.N, 1, 4), 0, 0, 0}};
   for (int i = 0; i < 4; ++i) {
     for (int j = i + 1; j < 4; ++j)
@@ -149,20 +156,20 @@ int validate(const fa_bwd_desc& a) {
 template <int D, bool CAUSAL, typename E, bool STRIDED>
 hipError_t launch(const fa::BwdParams& p0, hipStream_t stream) {
   fa::BwdParams p = p0;
-  const long long rows = (long long)p.BH * p.N;
+  const long long rows = (long long)p.BH * p.Nq;
   constexpr int kRowsPerBlock = 256 / (D / 8);
   const long long pre_blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   hipLaunchKernelGGL((fa::fa_bwd_pre_kernel<D, E, STRIDED>), dim3((unsigned)pre_blocks), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int kBK = kDkdvWaves<D> * 32;
-  p.ntiles = (p.N + kBK - 1) / kBK;
+  p.ntiles = (p.Nk + kBK - 1) / kBK;  // key tiles
   hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<D, CAUSAL, kDkdvWaves<D>, kDkdvVlds<D>, E, STRIDED>),
                      dim3((unsigned)(p.BH * p.ntiles)), dim3(kDkdvWaves<D> * 64), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int kBQ = kDqWaves * 32;
-  p.ntiles = (p.N + kBQ - 1) / kBQ;
+  p.ntiles = (p.Nq + kBQ - 1) / kBQ;  // query tiles
   hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<D, CAUSAL, kDqWaves, kDqBK<D>, E, STRIDED>),
                      dim3((unsigned)(p.BH * p.ntiles)), dim3(kDqWaves * 64), 0, stream, p);
   return hipGetLastError();
@@ -201,15 +208,17 @@ int run(const fa_bwd_desc& a) {
   p.dk_sb = a.dk_stride[0], p.dk_sh = a.dk_stride[1], p.dk_rs = (int)a.dk_stride[2];
   p.dv_sb = a.dv_stride[0], p.dv_sh = a.dv_stride[1], p.dv_rs = (int)a.dv_stride[2];
   p.l_sb = a.lse_stride[0], p.l_sh = a.lse_stride[1];
-  p.H = a.H, p.BH = a.B * a.H, p.N = a.N;
+  p.H = a.H, p.BH = a.B * a.H, p.Nq = a.N, p.Nk = key_rows(a);
+  p.nqt = (a.N + 63) / 64;
   p.qk_scale = (float)((double)a.scale * 1.4426950408889634);
   p.scale = a.scale;
   // Every tensor contiguous [B, H, N, d] (lse [B, H, N]): the kernels that
   // derive all addresses from (head, row).
   bool strided = a.lse_stride[1] != a.N || a.lse_stride[0] != (long long)a.H * a.N;
-  const long long* ts[8] = {a.q_stride,  a.k_stride,  a.v_stride,  a.o_stride,
-                            a.do_stride, a.dq_stride, a.dk_stride, a.dv_stride};
-  for (const long long* t : ts) strided = strided || !contiguous(t, a.H, a.N, a.d);
+  for (const long long* t : {a.q_stride, a.o_stride, a.do_stride, a.dq_stride})
+    strided = strided || !contiguous(t, a.H, a.N, a.d);
+  for (const long long* t : {a.k_stride, a.v_stride, a.dk_stride, a.dv_stride})
+    strided = strided || !contiguous(t, a.H, p.Nk, a.d);
   const hipStream_t s = static_cast<hipStream_t>(a.stream);
   hipError_t e;
   if (a.d == 64)

@@ -45,10 +45,11 @@ namespace fa {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
-// Kernel arguments of the backward.  Tensors are addressed by element strides
-// (batch, head, row) with a contiguous head dimension; the STRIDED = false
-// kernels assume contiguous [B, H, N, d] (lse [B, H, N]) and ignore them.  The
-// workspace holds lse2 and dsum, contiguous [B*H, N] fp32 each.
+// Kernel arguments of the backward: Nq query rows (q, out, dout, dq, lse) over
+// Nk key rows (k, v, dk, dv) per head.  Tensors are addressed by element
+// strides (batch, head, row) with a contiguous head dimension; the STRIDED =
+// false kernels assume contiguous [B, H, rows, d] (lse [B, H, Nq]) and ignore
+// them.  The workspace holds lse2 and dsum, contiguous [B*H, Nq] fp32 each.
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -64,19 +65,20 @@ struct BwdParams {
   long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh, do_sb, do_sh;
   long long dq_sb, dq_sh, dk_sb, dk_sh, dv_sb, dv_sh, l_sb, l_sh;
   int q_rs, k_rs, v_rs, o_rs, do_rs, dq_rs, dk_rs, dv_rs;
-  int H, BH, N, ntiles;
+  int H, BH, Nq, Nk, ntiles;
+  int nqt;  // query tiles of 64 rows per head: ceil(Nq / 64)
   float qk_scale;  // scale * log2(e)
   float scale;
 };
 
-// Element offset of head bh of a tensor: strided, or contiguous [B, H, N, D].
+// Element offset of head bh of a tensor: strided, or contiguous [B, H, rows, D].
 template <bool STRIDED, int D>
-__device__ __forceinline__ long long head_off(long long sb, long long sh, int bh, int H, int N) {
+__device__ __forceinline__ long long head_off(long long sb, long long sh, int bh, int H, int rows) {
   if constexpr (STRIDED) {
     const int b = bh / H;
     return b * sb + (bh - b * H) * sh;
   } else {
-    return (long long)bh * N * D;
+    return (long long)bh * rows * D;
   }
 }
 
@@ -187,17 +189,17 @@ __device__ __forceinline__ void tile_of(int i, int total, int BH, int ntiles, bo
 template <int D, typename E, bool STRIDED>
 __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const BwdParams pr) {
   constexpr int kLanes = D / 8;  // 16 bytes of a row per lane
-  const long long rows = (long long)pr.BH * pr.N;
+  const long long rows = (long long)pr.BH * pr.Nq;
   const long long r = (long long)blockIdx.x * (256 / kLanes) + threadIdx.x / kLanes;
   const int c = (threadIdx.x % kLanes) * 8;
   float acc = 0.f;
   int bh = 0, i = 0;
   if (r < rows) {
-    bh = (int)(r / pr.N);
-    i = (int)(r - (long long)bh * pr.N);
+    bh = (int)(r / pr.Nq);
+    i = (int)(r - (long long)bh * pr.Nq);
     const int o_rs = STRIDED ? pr.o_rs : D, do_rs = STRIDED ? pr.do_rs : D;
-    const uint16_t* orow = pr.out + head_off<STRIDED, D>(pr.o_sb, pr.o_sh, bh, pr.H, pr.N) + (long long)i * o_rs;
-    const uint16_t* grow = pr.dout + head_off<STRIDED, D>(pr.do_sb, pr.do_sh, bh, pr.H, pr.N) + (long long)i * do_rs;
+    const uint16_t* orow = pr.out + head_off<STRIDED, D>(pr.o_sb, pr.o_sh, bh, pr.H, pr.Nq) + (long long)i * o_rs;
+    const uint16_t* grow = pr.dout + head_off<STRIDED, D>(pr.do_sb, pr.do_sh, bh, pr.H, pr.Nq) + (long long)i * do_rs;
     const u32x4 o = *reinterpret_cast<const u32x4*>(orow + c);
     const u32x4 g = *reinterpret_cast<const u32x4*>(grow + c);
 #pragma unroll
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const BwdParams pr) {
   for (int m = kLanes / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kLanes);
   if (r < rows && c == 0) {
     pr.dsum[r] = acc;
-    const long long l_off = STRIDED ? (long long)(bh / pr.H) * pr.l_sb + (bh % pr.H) * pr.l_sh : (long long)bh * pr.N;
+    const long long l_off = STRIDED ? (long long)(bh / pr.H) * pr.l_sb + (bh % pr.H) * pr.l_sh : (long long)bh * pr.Nq;
     pr.lse2[r] = pr.lse[l_off + i] * kLog2e;
   }
 }
@@ -236,7 +238,7 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
   __shared__ __attribute__((aligned(1024))) char lds1[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char vlds[kVBytes];
 
-  const int N = pr.N;
+  const int Nq = pr.Nq, Nk = pr.Nk;
   const float qk_scale = pr.qk_scale;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -247,13 +249,22 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
   const int q_rs = STRIDED ? pr.q_rs : D, do_rs = STRIDED ? pr.do_rs : D;
   const int k_rs = STRIDED ? pr.k_rs : D, v_rs = STRIDED ? pr.v_rs : D;
   const __amdgpu_buffer_rsrc_t qrs =
-      make_rsrc(pr.q + head_off<STRIDED, D>(pr.q_sb, pr.q_sh, bh, pr.H, N), (uint32_t)((N - 1) * q_rs + D) * 2);
-  const __amdgpu_buffer_rsrc_t drs =
-      make_rsrc(pr.dout + head_off<STRIDED, D>(pr.do_sb, pr.do_sh, bh, pr.H, N), (uint32_t)((N - 1) * do_rs + D) * 2);
-  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(pr.lse2 + (long long)bh * N, (uint32_t)N * 4);
-  const __amdgpu_buffer_rsrc_t srs = make_rsrc(pr.dsum + (long long)bh * N, (uint32_t)N * 4);
+      make_rsrc(pr.q + head_off<STRIDED, D>(pr.q_sb, pr.q_sh, bh, pr.H, Nq), (uint32_t)((Nq - 1) * q_rs + D) * 2);
+  const __amdgpu_buffer_rsrc_t drs = make_rsrc(pr.dout + head_off<STRIDED, D>(pr.do_sb, pr.do_sh, bh, pr.H, Nq),
+                                               (uint32_t)((Nq - 1) * do_rs + D) * 2);
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(pr.lse2 + (long long)bh * Nq, (uint32_t)Nq * 4);
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(pr.dsum + (long long)bh * Nq, (uint32_t)Nq * 4);
   const int k0 = kt * kBK;
   const int kw = k0 + wave * 32;  // first key of this wavefront
+  // Causal (top-left: key j is seen by queries i >= j): queries before k0 see
+  // none of these keys, and when k0 >= Nq no query does (then no tile is
+  // staged and dK = dV = 0 are written).
+  // (Non-causal, the count is pr.nqt; the strided kernel takes it from there,
+  // where its registers allocate with a quarter of the spill of the computed
+  // form, 52 against 208 bytes per lane at d = 128.)
+  static_assert(BQ == 64, "pr.nqt counts 64-row query tiles");
+  const int qbeg = CAUSAL ? k0 : 0;
+  const int ntiles = (STRIDED && !CAUSAL) ? pr.nqt : (qbeg < Nq ? (Nq - qbeg + BQ - 1) / BQ : 0);
 
   using Dma = BlockDma<D, WAVES>;
   const uint32_t dma_q = Dma::lane_off(lane, wave, q_rs), dma_d = Dma::lane_off(lane, wave, do_rs);
@@ -267,9 +278,9 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
   v8 kreg[D / 16], vreg[VLDS ? 1 : D / 16];
   {
     const __amdgpu_buffer_rsrc_t krs =
-        make_rsrc(pr.k + head_off<STRIDED, D>(pr.k_sb, pr.k_sh, bh, pr.H, N), (uint32_t)((N - 1) * k_rs + D) * 2);
+        make_rsrc(pr.k + head_off<STRIDED, D>(pr.k_sb, pr.k_sh, bh, pr.H, Nk), (uint32_t)((Nk - 1) * k_rs + D) * 2);
     const __amdgpu_buffer_rsrc_t vrs =
-        make_rsrc(pr.v + head_off<STRIDED, D>(pr.v_sb, pr.v_sh, bh, pr.H, N), (uint32_t)((N - 1) * v_rs + D) * 2);
+        make_rsrc(pr.v + head_off<STRIDED, D>(pr.v_sb, pr.v_sh, bh, pr.H, Nk), (uint32_t)((Nk - 1) * v_rs + D) * 2);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const uint32_t koff = ((kw + lr) * k_rs + ks * 16 + g * 8) * 2;
@@ -280,8 +291,8 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
       }
     }
     if constexpr (VLDS) {
-      // kBK rows of V, swizzled like a tile; rows >= N read 0.  Waited for with
-      // the first Q / dO tile.
+      // kBK rows of V, swizzled like a tile; rows >= Nk read 0.  Waited for
+      // with the first Q / dO tile (or below, when there is none).
       constexpr int kVBlocksPerWave = kVBytes / 1024 / WAVES;
       const uint32_t dma_v = Dma::lane_off(lane, wave, v_rs);
 #pragma unroll
@@ -296,9 +307,6 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dk[db] = dv[db] = f32x16{};
 
-  // Causal: queries before k0 see none of these keys.
-  const int qbeg = CAUSAL ? k0 : 0;
-  const int ntiles = (N - qbeg + BQ - 1) / BQ;
 
   auto issue_tile = [&](int j, int stage) {
     const int qs = qbeg + j * BQ;
@@ -390,7 +398,9 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
     __syncthreads();                     // ... every wave's, and this stage is free
   };
 
-  issue_tile(0, 0);  // ntiles >= 1: k0 < N
+  if (ntiles > 0) issue_tile(0, 0);  // uniform over the workgroup
+  // The first tile (and V) landed for every wave; with no tile, the V load is
+  // drained before the workgroup's LDS is released.
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   int j = 0;
@@ -402,10 +412,10 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
 
   // ---- epilogue: dK = scale * (dK^T)^T, dV -> E --------------------------------
   const int key = kw + lr;
-  if (key < N) {
+  if (key < Nk) {
     const int dk_rs = STRIDED ? pr.dk_rs : D, dv_rs = STRIDED ? pr.dv_rs : D;
-    uint16_t* krow = pr.dk + head_off<STRIDED, D>(pr.dk_sb, pr.dk_sh, bh, pr.H, N) + (long long)key * dk_rs;
-    uint16_t* vout = pr.dv + head_off<STRIDED, D>(pr.dv_sb, pr.dv_sh, bh, pr.H, N) + (long long)key * dv_rs;
+    uint16_t* krow = pr.dk + head_off<STRIDED, D>(pr.dk_sb, pr.dk_sh, bh, pr.H, Nk) + (long long)key * dk_rs;
+    uint16_t* vout = pr.dv + head_off<STRIDED, D>(pr.dv_sb, pr.dv_sh, bh, pr.H, Nk) + (long long)key * dv_rs;
     const float sc = pr.scale;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -436,7 +446,7 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams p
   __shared__ __attribute__((aligned(1024))) char lds0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char lds1[kStageBytes];
 
-  const int N = pr.N, nqt = pr.ntiles;
+  const int Nq = pr.Nq, Nk = pr.Nk, nqt = pr.ntiles;
   const float qk_scale = pr.qk_scale;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -448,9 +458,9 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams p
   const int q_rs = STRIDED ? pr.q_rs : D, do_rs = STRIDED ? pr.do_rs : D;
   const int k_rs = STRIDED ? pr.k_rs : D, v_rs = STRIDED ? pr.v_rs : D;
   const __amdgpu_buffer_rsrc_t krs =
-      make_rsrc(pr.k + head_off<STRIDED, D>(pr.k_sb, pr.k_sh, bh, pr.H, N), (uint32_t)((N - 1) * k_rs + D) * 2);
+      make_rsrc(pr.k + head_off<STRIDED, D>(pr.k_sb, pr.k_sh, bh, pr.H, Nk), (uint32_t)((Nk - 1) * k_rs + D) * 2);
   const __amdgpu_buffer_rsrc_t vrs =
-      make_rsrc(pr.v + head_off<STRIDED, D>(pr.v_sb, pr.v_sh, bh, pr.H, N), (uint32_t)((N - 1) * v_rs + D) * 2);
+      make_rsrc(pr.v + head_off<STRIDED, D>(pr.v_sb, pr.v_sh, bh, pr.H, Nk), (uint32_t)((Nk - 1) * v_rs + D) * 2);
   const int q0 = qt * kBQ;
   const int qw = q0 + wave * 32;
   const int query = qw + lr;
@@ -459,9 +469,9 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams p
   v8 qreg[D / 16], doreg[D / 16];
   {
     const __amdgpu_buffer_rsrc_t qrs =
-        make_rsrc(pr.q + head_off<STRIDED, D>(pr.q_sb, pr.q_sh, bh, pr.H, N), (uint32_t)((N - 1) * q_rs + D) * 2);
-    const __amdgpu_buffer_rsrc_t drs = make_rsrc(pr.dout + head_off<STRIDED, D>(pr.do_sb, pr.do_sh, bh, pr.H, N),
-                                                 (uint32_t)((N - 1) * do_rs + D) * 2);
+        make_rsrc(pr.q + head_off<STRIDED, D>(pr.q_sb, pr.q_sh, bh, pr.H, Nq), (uint32_t)((Nq - 1) * q_rs + D) * 2);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(pr.dout + head_off<STRIDED, D>(pr.do_sb, pr.do_sh, bh, pr.H, Nq),
+                                                 (uint32_t)((Nq - 1) * do_rs + D) * 2);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const uint32_t qoff = (query * q_rs + ks * 16 + g * 8) * 2;
@@ -471,9 +481,9 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams p
     }
   }
   float l2 = 0.f, dd = 0.f;
-  if (query < N) {
-    l2 = pr.lse2[(long long)bh * N + query];
-    dd = pr.dsum[(long long)bh * N + query];
+  if (query < Nq) {
+    l2 = pr.lse2[(long long)bh * Nq + query];
+    dd = pr.dsum[(long long)bh * Nq + query];
   }
 
   using Dma = BlockDma<D, WAVES>;
@@ -488,7 +498,7 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams p
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
 
-  const int kend = CAUSAL ? min(q0 + kBQ, N) : N;
+  const int kend = CAUSAL ? min(q0 + kBQ, Nk) : Nk;
   const int ntiles = (kend + BK - 1) / BK;
 
   auto issue_tile = [&](int j, int stage) {
@@ -528,7 +538,7 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams p
         float p = __builtin_amdgcn_exp2f(fmaf(s[r], qk_scale, -l2));
         if (masked) {
           const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if ((CAUSAL && key > query) || key >= N) p = 0.f;
+          if ((CAUSAL && key > query) || key >= Nk) p = 0.f;
         }
         dp[r] = p * (dp[r] - dd);
       }
@@ -549,13 +559,13 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams p
     if (j + 1 < ntiles) issue_tile(j + 1, stage ^ 1);
     const int k0 = j * BK;
     const bool skip = CAUSAL && (k0 > qw + 31);
-    const bool masked = (CAUSAL && (k0 + BK - 1 > qw)) || (k0 + BK > N);
+    const bool masked = (CAUSAL && (k0 + BK - 1 > qw)) || (k0 + BK > Nk);
     if (!skip) compute_tile(stage ? lds1 : lds0, k0, masked);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   };
 
-  issue_tile(0, 0);  // ntiles >= 1: q0 < N
+  issue_tile(0, 0);  // ntiles >= 1: kend >= 1
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   int j = 0;
@@ -565,9 +575,9 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams p
   }
   if (j < ntiles) step(j, 0);
 
-  if (query < N) {
+  if (query < Nq) {
     const int dq_rs = STRIDED ? pr.dq_rs : D;
-    uint16_t* row = pr.dq + head_off<STRIDED, D>(pr.dq_sb, pr.dq_sh, bh, pr.H, N) + (long long)query * dq_rs;
+    uint16_t* row = pr.dq + head_off<STRIDED, D>(pr.dq_sb, pr.dq_sh, bh, pr.H, Nq) + (long long)query * dq_rs;
     const float sc = pr.scale;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)

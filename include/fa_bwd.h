@@ -62,18 +62,26 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
            long long workspace_bytes, void* stream);
 
 /*
- * General layouts and fp16: the operation of fa_bwd on tensors addressed by
- * element strides (the head dimension contiguous), in bfloat16 or IEEE fp16.
- * Heads stay square (every tensor has N rows per head); the mask and the
- * formulas are those of fa_bwd.
+ * General layouts, lengths and fp16: the operation of fa_bwd on tensors
+ * addressed by element strides (the head dimension contiguous), in bfloat16 or
+ * IEEE fp16, for N query rows over Nk key rows per head.  The formulas are
+ * those of fa_bwd; the mask is fa_fwd_ex's: A(i) = all Nk keys, or when causal
+ * {j < Nk : j <= i} (top-left alignment; with N < Nk the keys j >= N are seen by
+ * no query and get dk = dv = 0).  out and lse must be fa_fwd_ex's outputs for
+ * the same lengths, scale and mask.
  *
- *   q, k, v, out, dout   read only; element (b, h, i, c) of q at
+ *   q, out, dout         read only, i < N rows per head; element (b, h, i, c)
+ *                        of q at
  *                        q[b*q_stride[0] + h*q_stride[1] + i*q_stride[2] + c],
  *                        and likewise for each tensor with its own strides.
  *                        A [B, N, H, d] tensor has strides {N*H*d, d, H*d}.
+ *   k, v                 read only, Nk rows per head, addressed the same way.
  *   lse                  fp32, element (b, h, i) at
  *                        lse[b*lse_stride[0] + h*lse_stride[1] + i].  Read only.
- *   dq, dk, dv           written, every element, with their own strides.
+ *   dq                   written, N rows per head; dk, dv written, Nk rows;
+ *                        every element, with their own strides.
+ *   Nk                   key rows per head; 0 means Nk = N (so a zero-
+ *                        initialised descriptor keeps square heads).
  *   dtype                FA_DTYPE_BF16 (0) or FA_DTYPE_F16 for all nine 16-bit
  *                        tensors alike (else FA_ERR_ARG); products accumulate in
  *                        fp32 and P, dS enter the matrix instruction in dtype.
@@ -81,9 +89,11 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
  *   workspace            as for fa_bwd (fa_bwd_workspace_bytes(B, H, N, d)).
  * Stride rules (else FA_ERR_STRIDE): those of fa_fwd_desc for 16-bit
  * elements: every stride >= 0 and a multiple of 8 elements, every row stride
- * >= d, (N + 256) * row stride < 2^30; lse strides >= 0.
+ * >= d, (rows + 256) * row stride < 2^30 with each tensor's own row count; lse
+ * strides >= 0.  The workspace is sized by the query rows:
+ * fa_bwd_workspace_bytes(B, H, N, d).
  * Errors, in this order: FA_ERR_NULL (desc or a pointer), FA_ERR_SHAPE (B, H,
- * N < 1, or B*H*N >= 2^31), FA_ERR_HEAD_DIM, FA_ERR_STRIDE, FA_ERR_SCALE,
+ * N or Nk < 1, or B*H*max(N, Nk) >= 2^31), FA_ERR_HEAD_DIM, FA_ERR_STRIDE, FA_ERR_SCALE,
  * FA_ERR_ARG (causal, dtype), FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_ALIAS
  * (judged on each tensor's whole byte extent, as for fa_bwd), FA_ERR_NO_DEVICE,
  * FA_ERR_LAUNCH.  When every tensor is contiguous [B, H, N, d] (lse [B, H, N])
@@ -104,6 +114,7 @@ typedef struct fa_bwd_desc {
   void *workspace;
   long long workspace_bytes;
   void *stream;
+  int Nk;
 } fa_bwd_desc;
 
 int fa_bwd_ex(const fa_bwd_desc *desc);

@@ -376,3 +376,29 @@ def test_bwd_ex_valid_layouts_reach_the_device_check(lib):
     assert bwd_ex(lib, B=B, N=N, H=H, d=d, q_stride=bnhd, k_stride=bnhd, v_stride=bnhd, o_stride=bnhd,
                   do_stride=bnhd, dq_stride=bnhd, dk_stride=bnhd, dv_stride=bnhd, lse_stride=(2 * N * H, 2 * N),
                   dtype=1) == 8
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Nk=-1), 2),
+    (dict(Nk=1 << 30), 2),                                            # B*H*Nk = 2^31
+    # (Nk + 256) * row stride * 2 bytes >= 2^31 for k, although fine for N = 64 rows
+    (dict(Nk=1 << 20, k_stride=(1 << 31, 1 << 30, 1024)), 11),
+])
+def test_bwd_ex_key_length_errors(lib, kw, code):
+    assert bwd_ex(lib, **kw) == code
+
+
+def test_bwd_ex_non_square_reaches_the_device_check(lib):
+    """Nq = 64 queries over Nk = 300 keys: k, v, dk, dv take Nk rows; the alias
+    check uses each tensor's own extent (dk placed right after a 64-row dq is
+    fine, right after a 300-row dq it would not be)."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    H, N, Nk, d = 2, 64, 300, 64
+    qs, ks = (H * N * d, N * d, d), (H * Nk * d, Nk * d, d)
+    kw = dict(N=N, Nk=Nk, H=H, d=d, q_stride=qs, o_stride=qs, do_stride=qs, dq_stride=qs, k_stride=ks,
+              v_stride=ks, dk_stride=ks, dv_stride=ks, lse_stride=(H * N, N))
+    assert bwd_ex(lib, **kw) == 8
+    assert bwd_ex(lib, **dict(kw, dk=7 * FAKE + H * N * d * 2)) == 8      # just after dq's extent
+    assert bwd_ex(lib, **dict(kw, dk=7 * FAKE + H * N * d * 2 - 16)) == 7  # overlaps dq's last row

@@ -162,3 +162,54 @@ def test_f16_long_head_matches_oracle(N, d, causal):
     torch.cuda.synchronize()
     oracle_check([bits_of(g) for g in grads], q, k, v, dout, scale, causal, "f16",
                  "bwd f16 N%d d%d c%d" % (N, d, causal))
+
+
+def problem_qk(seed, B, H, Nq, Nk, d, dtype):
+    q, _, _ = random_qkv(seed, B, H, Nq, d, dtype=dtype)
+    _, k, v = random_qkv(seed + 1, B, H, Nk, d, dtype=dtype)
+    dout = normal_bits(seed + 3, B * H * Nq * d, dtype=dtype).reshape(B, H, Nq, d)
+    return q, k, v, dout
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("Nq,Nk", [(100, 300), (300, 100), (1, 517), (517, 33), (64, 600)])
+def test_non_square_matches_oracle(Nq, Nk, d, causal):
+    """Nq queries over Nk keys (top-left causal), against the oracle; with
+    causal and Nq < Nk the keys j >= Nq are seen by no query and their dk, dv
+    rows must be exactly zero."""
+    import torch
+    import flashattention_forward_fa2_amd as fa
+    B, H = 1, 2
+    q, k, v, dout = problem_qk(9900 + Nq + Nk + d + causal, B, H, Nq, Nk, d, "bf16")
+    scale = fp32_scale(d)
+    tq, tk, tv, tg = (to_device(a) for a in (q, k, v, dout))
+    out, lse = fa.fa_fwd_ex(tq, tk, tv, scale=scale, causal=bool(causal))
+    grads = fa.fa_bwd_ex(tq, tk, tv, out, lse, tg, scale=scale, causal=bool(causal))
+    torch.cuda.synchronize()
+    got = [bits_of(g) for g in grads]
+    assert got[0].shape == (B, H, Nq, d) and got[1].shape == got[2].shape == (B, H, Nk, d)
+    oracle_check(got, q, k, v, dout, scale, causal, "bf16", "bwd Nq%d Nk%d d%d c%d" % (Nq, Nk, d, causal))
+    if causal and Nq < Nk:
+        assert not np.any(got[1][:, :, Nq:]) and not np.any(got[2][:, :, Nq:])
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_non_square_strided_f16(causal):
+    """fp16, [B, N, H, d] memory for every tensor, 200 queries over 77 keys."""
+    import torch
+    import flashattention_forward_fa2_amd as fa
+    B, H, Nq, Nk, d = 2, 3, 200, 77, 64
+    q, k, v, dout = problem_qk(9950 + causal, B, H, Nq, Nk, d, "f16")
+    scale = fp32_scale(d)
+    tq, tk, tv, tg = (bnhd_view(a, "f16") for a in (q, k, v, dout))
+    out = torch.empty((B, Nq, H, d), dtype=torch.float16, device=tq.device).transpose(1, 2)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=tq.device)
+    fa.fa_fwd_ex(tq, tk, tv, scale=scale, causal=bool(causal), out=out, lse=lse)
+    dq = torch.full((B, Nq, H, d), float("nan"), dtype=torch.float16, device=tq.device).transpose(1, 2)
+    dk, dv = (torch.full((B, Nk, H, d), float("nan"), dtype=torch.float16, device=tq.device).transpose(1, 2)
+              for _ in range(2))
+    fa.fa_bwd_ex(tq, tk, tv, out, lse, tg, scale=scale, causal=bool(causal), dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    oracle_check([bits_of(g) for g in (dq, dk, dv)], q, k, v, dout, scale, causal, "f16",
+                 "bwd f16 [B,N,H,d] Nq%d Nk%d c%d" % (Nq, Nk, causal))
