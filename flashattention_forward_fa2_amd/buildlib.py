@@ -60,5 +60,46 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+def resource_usage() -> list[dict]:
+    """Per-kernel resources of the device code as the library builds it (the
+    compiler's kernel-resource-usage remarks): one dict per kernel with its
+    demangled name, VGPRs, AGPRs, scratch bytes per lane, waves per SIMD and
+    LDS bytes per workgroup."""
+    import re
+    fields = {"VGPRs": "vgpr", "AGPRs": "agpr", "ScratchSize [bytes/lane]": "scratch",
+              "Occupancy [waves/SIMD]": "waves", "LDS Size [bytes/block]": "lds"}
+    out = []
+    for src in SOURCES:
+        cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "--cuda-device-only", "-c",
+               "-Rpass-analysis=kernel-resource-usage", "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS,
+               "-o", os.devnull, os.path.join(CSRC, src)]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc failed on %s:\n%s" % (src, res.stderr[-2000:]))
+        cur = None
+        for line in res.stderr.splitlines():
+            m = re.search(r"Function Name: (\S+)", line)
+            if m:
+                cur = {"mangled": m.group(1), "source": src}
+                out.append(cur)
+                continue
+            for label, key in fields.items():
+                m = re.search(re.escape(label) + r": (\d+)", line)
+                if m and cur is not None:
+                    cur[key] = int(m.group(1))
+    names = subprocess.run(["c++filt"], input="\n".join(k["mangled"] for k in out), capture_output=True,
+                           text=True).stdout.splitlines()
+    for k, n in zip(out, names):
+        k["name"] = n.replace("fa::", "").replace("(fa::Params)", "").replace("(fa::BwdParams)", "")
+    return out
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if sys.argv[1:] == ["--resources"]:
+        print("| kernel | VGPR | AGPR | scratch B/lane | waves/SIMD | LDS B |")
+        print("|---|---|---|---|---|---|")
+        for k in resource_usage():
+            print("| `%s` | %d | %d | %d | %d | %d |" % (k["name"], k.get("vgpr", 0), k.get("agpr", 0),
+                                                        k.get("scratch", 0), k.get("waves", 0), k.get("lds", 0)))
+    else:
+        print(build(verbose=True))
