@@ -214,7 +214,7 @@ def main():
             tflops=round(tf, 2),
             frac_of_peak=round(tf / peak, 4),
             hbm_gbs=round((4.0 * B * H * N * d + 4.0 * B * H * Nk * d + 4.0 * B * H * N) / (avg * 1e-3) / 1e9, 1),
-            cfg=list(cfg if cfg else ((1, 4, 32) if args.dtype == "f32" else fa.default_cfg(N, d, bool(c)))))
+            cfg=list(cfg if cfg else fa.launch_cfg(B, H, N, d, bool(c), args.dtype)))
     # Outside the timed region: each mode again with the caches flushed before
     # every launch (a 512 MiB write, more than L2 and the 256 MB Infinity Cache).
     if args.flush_reps > 0:

@@ -15,11 +15,11 @@ from .buildlib import LIB, build  # noqa: F401
 
 __all__ = ["fa_fwd", "fa_fwd_ptr", "fa_fwd_cfg", "fa_fwd_ex", "fa_fwd_ex_ptr", "fa_fwd_splitkv",
            "splitkv_workspace_bytes", "splitkv_default_splits", "FwdDesc", "FaError", "strerror",
-           "version", "default_cfg", "variants", "load_library", "EXPORTED_SYMBOLS", "fa_bwd", "fa_bwd_ptr",
+           "version", "default_cfg", "launch_cfg", "variants", "load_library", "EXPORTED_SYMBOLS", "fa_bwd", "fa_bwd_ptr",
            "bwd_workspace_bytes", "fa_bwd_ex", "fa_bwd_ex_ptr", "BwdDesc"]
 
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_cfg", "fa_fwd_ex", "fa_fwd_ex_cfg", "fa_fwd_splitkv",
-                    "fa_splitkv_workspace_bytes", "fa_splitkv_default_splits", "fa_default_cfg", "fa_num_variants",
+                    "fa_splitkv_workspace_bytes", "fa_splitkv_default_splits", "fa_default_cfg", "fa_launch_cfg", "fa_num_variants",
                     "fa_variant", "fa_variant_dtype", "fa_strerror", "fa_version", "fa_bwd", "fa_bwd_ex",
                     "fa_bwd_workspace_bytes")
 
@@ -118,6 +118,8 @@ def load_library():
             lib.fa_splitkv_default_splits.restype = _I
             lib.fa_default_cfg.argtypes = [_I, _I, _I, ctypes.POINTER(TileCfg)]
             lib.fa_default_cfg.restype = _I
+            lib.fa_launch_cfg.argtypes = [_I, _I, _I, _I, _I, _I, ctypes.POINTER(TileCfg)]
+            lib.fa_launch_cfg.restype = _I
             lib.fa_num_variants.argtypes = []
             lib.fa_num_variants.restype = _I
             lib.fa_variant.argtypes = [_I, ctypes.POINTER(_I), ctypes.POINTER(_I), ctypes.POINTER(TileCfg)]
@@ -154,6 +156,14 @@ def _check(status: int):
 def default_cfg(N: int, d: int, causal: bool):
     c = TileCfg()
     _check(load_library().fa_default_cfg(int(N), int(d), int(bool(causal)), ctypes.byref(c)))
+    return c.as_tuple()
+
+
+def launch_cfg(B: int, H: int, Nq: int, d: int, causal: bool, dtype: str = "bf16"):
+    """The ``(qb, waves, bk)`` tile fa_fwd / fa_fwd_ex launch for these sizes on the current device."""
+    c = TileCfg()
+    _check(load_library().fa_launch_cfg(int(B), int(H), int(Nq), int(d), int(bool(causal)), _DTYPE_NAMES[dtype],
+                                        ctypes.byref(c)))
     return c.as_tuple()
 
 

@@ -154,19 +154,34 @@ int validate(const void* q, const void* k, const void* v, const void* out, const
   return FA_OK;
 }
 
-// Per-device "is this a gfx950" cache, filled once per device.
+// Per-device "is this a gfx950" and compute-unit count cache, filled once per
+// device.
 constexpr int kMaxDevices = 64;
 std::once_flag g_dev_once[kMaxDevices];
 int g_dev_ok[kMaxDevices];
+int g_dev_cus[kMaxDevices];
 
-int check_device() {
+// FA_OK with *cus = the current device's compute units, or FA_ERR_NO_DEVICE.
+int check_device(int* cus = nullptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_NO_DEVICE;
   std::call_once(g_dev_once[dev], [dev] {
     hipDeviceProp_t p;
     g_dev_ok[dev] = hipGetDeviceProperties(&p, dev) == hipSuccess && std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    g_dev_cus[dev] = g_dev_ok[dev] ? p.multiProcessorCount : 0;
   });
+  if (cus) *cus = g_dev_cus[dev];
   return g_dev_ok[dev] ? FA_OK : FA_ERR_NO_DEVICE;
+}
+
+// The tile a launch uses when the caller names none: default_cfg_dt, except
+// that an 8-wavefront grid smaller than the GPU (B*H*ceil(Nq/256) workgroups,
+// one per CU at a time) takes 4-wavefront tiles, which doubles its workgroups.
+fa_tile_cfg launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, int cus) {
+  fa_tile_cfg c = default_cfg_dt(Nq, d, causal, dtype);
+  const long long wgs = (long long)B * H * ((Nq + c.qb * c.waves * 32 - 1) / (c.qb * c.waves * 32));
+  if (c.waves == 8 && wgs < cus) c = fa_tile_cfg{1, 4, 64};
+  return c;
 }
 
 // Byte extent of a strided [B, H, N, d] tensor: from its base to one past its
@@ -237,13 +252,17 @@ fa::Params make_params(const fa_fwd_desc& a) {
   return p;
 }
 
-int run_desc(const fa_fwd_desc& a, const fa_tile_cfg& cfg) {
+// cfg = nullptr: launch_cfg's choice for this device.
+int run_desc(const fa_fwd_desc& a, const fa_tile_cfg* cfg) {
   const int st = validate_desc(a);
   if (st != FA_OK) return st;
-  const Variant* var = find_variant(a.d, a.causal, cfg, a.dtype);
-  if (!var) return FA_ERR_ARG;
-  const int dst = check_device();
+  if (cfg && !find_variant(a.d, a.causal, *cfg, a.dtype)) return FA_ERR_ARG;
+  int cus = 0;
+  const int dst = check_device(&cus);
   if (dst != FA_OK) return dst;
+  const Variant* var =
+      find_variant(a.d, a.causal, cfg ? *cfg : launch_cfg(a.B, a.H, a.Nq, a.d, a.causal, a.dtype, cus), a.dtype);
+  if (!var) return FA_ERR_INTERNAL;
   fa::Params p = make_params(a);
   auto contiguous = [&](const long long st[3], int n) {
     return st[0] == (long long)a.H * n * a.d && st[1] == (long long)n * a.d && st[2] == a.d;
@@ -337,7 +356,7 @@ fa_fwd_desc square_desc(const void* q, const void* k, const void* v, void* out, 
 }
 
 int run(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int N, int d,
-        float scale, int causal, void* stream, const fa_tile_cfg& cfg) {
+        float scale, int causal, void* stream, const fa_tile_cfg* cfg) {
   const int st = validate(q, k, v, out, lse, B, H, N, d, scale, causal);
   if (st != FA_OK) return st;
   return run_desc(square_desc(q, k, v, out, lse, B, H, N, d, scale, causal, stream), cfg);
@@ -350,7 +369,7 @@ extern "C" {
 int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int N, int d,
            float scale, int causal, void* stream) {
   try {
-    return run(q, k, v, out, lse, B, H, N, d, scale, causal, stream, default_cfg(N, d, causal));
+    return run(q, k, v, out, lse, B, H, N, d, scale, causal, stream, nullptr);
   } catch (...) {
     return FA_ERR_INTERNAL;
   }
@@ -360,7 +379,7 @@ int fa_fwd_cfg(const void* q, const void* k, const void* v, void* out, float* ls
                float scale, int causal, void* stream, const fa_tile_cfg* cfg) {
   if (!cfg) return FA_ERR_ARG;
   try {
-    return run(q, k, v, out, lse, B, H, N, d, scale, causal, stream, *cfg);
+    return run(q, k, v, out, lse, B, H, N, d, scale, causal, stream, cfg);
   } catch (...) {
     return FA_ERR_INTERNAL;
   }
@@ -369,7 +388,7 @@ int fa_fwd_cfg(const void* q, const void* k, const void* v, void* out, float* ls
 int fa_fwd_ex(const fa_fwd_desc* desc) {
   if (!desc) return FA_ERR_NULL;
   try {
-    return run_desc(*desc, default_cfg_dt(desc->Nk, desc->d, desc->causal, desc->dtype));
+    return run_desc(*desc, nullptr);
   } catch (...) {
     return FA_ERR_INTERNAL;
   }
@@ -379,7 +398,7 @@ int fa_fwd_ex_cfg(const fa_fwd_desc* desc, const fa_tile_cfg* cfg) {
   if (!desc) return FA_ERR_NULL;
   if (!cfg) return FA_ERR_ARG;
   try {
-    return run_desc(*desc, *cfg);
+    return run_desc(*desc, cfg);
   } catch (...) {
     return FA_ERR_INTERNAL;
   }
@@ -404,6 +423,22 @@ int fa_fwd_splitkv(const fa_fwd_desc* desc, int num_splits, void* workspace, lon
   if (!desc) return FA_ERR_NULL;
   try {
     return run_splitkv(*desc, num_splits, workspace, workspace_bytes);
+  } catch (...) {
+    return FA_ERR_INTERNAL;
+  }
+}
+
+int fa_launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, fa_tile_cfg* cfg) {
+  if (!cfg) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Nq < 1) return FA_ERR_SHAPE;
+  if (!head_dim_ok(d) || (dtype == FA_DTYPE_F32 && d != 64 && d != 128)) return FA_ERR_HEAD_DIM;
+  if ((causal != 0 && causal != 1) || dtype < FA_DTYPE_BF16 || dtype > FA_DTYPE_F32) return FA_ERR_ARG;
+  try {
+    int cus = 0;
+    const int st = check_device(&cus);
+    if (st != FA_OK) return st;
+    *cfg = launch_cfg(B, H, Nq, d, causal, dtype, cus);
+    return FA_OK;
   } catch (...) {
     return FA_ERR_INTERNAL;
   }

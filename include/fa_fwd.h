@@ -176,8 +176,17 @@ long long fa_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int nu
  * (The split path runs 128-query workgroups when Nq <= 128, else fa_fwd's tile.) */
 int fa_splitkv_default_splits(int B, int H, int Nq, int Nk, int d, int causal);
 
-/* The configuration fa_fwd picks for (N, d, causal); FA_OK or an error code. */
+/* The configuration for (N, d, causal) on a grid that gives every compute unit
+ * a workgroup; FA_OK or an error code.  (Host only; no device needed.) */
 int fa_default_cfg(int N, int d, int causal, fa_tile_cfg *cfg);
+
+/* The configuration fa_fwd and fa_fwd_ex pick for these sizes and element type
+ * on the current device: fa_default_cfg's, except that when its 8-wavefront
+ * grid (B*H*ceil(Nq/256) workgroups) is smaller than the device's compute-unit
+ * count, the 4-wavefront tile (1, 4, 64), which doubles the workgroups.
+ * FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_ARG (causal, dtype)
+ * or FA_ERR_NO_DEVICE. */
+int fa_launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, fa_tile_cfg *cfg);
 
 /* Number of compiled variants, the i-th one (for d, causal given), and its
  * element type (an fa_dtype, or minus an error code).  fa_fwd and fa_fwd_cfg

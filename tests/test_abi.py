@@ -402,3 +402,21 @@ def test_bwd_ex_non_square_reaches_the_device_check(lib):
     assert bwd_ex(lib, **kw) == 8
     assert bwd_ex(lib, **dict(kw, dk=7 * FAKE + H * N * d * 2)) == 8      # just after dq's extent
     assert bwd_ex(lib, **dict(kw, dk=7 * FAKE + H * N * d * 2 - 16)) == 7  # overlaps dq's last row
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 1, 64, 64, 0, 0), 2), ((1, 1, 0, 64, 0, 0), 2), ((1, 1, 64, 96, 0, 0), 3), ((1, 1, 64, 32, 0, 2), 3),
+    ((1, 1, 64, 64, 2, 0), 5), ((1, 1, 64, 64, 0, 3), 5),
+])
+def test_launch_cfg_argument_errors(lib, args, code):
+    c = fa.TileCfg()
+    assert lib.fa_launch_cfg(*args, ctypes.byref(c)) == code
+
+
+def test_launch_cfg_needs_a_device(lib):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    c = fa.TileCfg()
+    assert lib.fa_launch_cfg(4, 8, 4096, 64, 0, 0, ctypes.byref(c)) == 8
+    assert lib.fa_launch_cfg(4, 8, 4096, 64, 0, 0, None) == 1

@@ -1,0 +1,48 @@
+"""The tile fa_fwd picks on its own (fa_launch_cfg): 8-wavefront tiles when the
+grid fills the GPU, 4-wavefront tiles when it would not, and the default launch
+is bit-identical to the explicit launch of the configuration it names."""
+import numpy as np
+import pytest
+
+from inputs import random_qkv
+from parity import fp32_scale, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import flashattention_forward_fa2_amd as fa
+    fa.load_library()
+    return torch.device("cuda:0")
+
+
+def test_choice_follows_the_grid():
+    import torch
+    import flashattention_forward_fa2_amd as fa
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert fa.launch_cfg(4, 8, 4096, 64, False) == (1, 8, 64)          # 512 workgroups of 256 queries
+    assert fa.launch_cfg(1, 8, 1024, 64, True) == (1, 4, 64)           # 32 of them: fewer than the CUs
+    assert fa.launch_cfg(1, 8, 1024, 128, False, "f16") == (1, 4, 64)
+    assert fa.launch_cfg(1, 8, 1024, 256, False) == (1, 4, 32)         # d = 256 has the 4-wave tile only
+    assert fa.launch_cfg(1, 8, 1024, 64, False, "f32") == (1, 4, 32)
+    n = 256 * ((cus + 7) // 8)                                         # 8 heads x n/256 tiles >= cus
+    assert fa.launch_cfg(1, 8, n, 64, False) == (1, 8, 64)
+    assert fa.launch_cfg(1, 8, n - 256, 64, False) == (1, 4, 64)      # 8 * (ceil(cus / 8) - 1) < cus
+
+
+@pytest.mark.parametrize("N,causal", [(1024, True), (1024, False), (4096, False)])
+def test_default_launch_equals_the_named_configuration(N, causal):
+    import torch
+    import flashattention_forward_fa2_amd as fa
+    B, H, d = 1, 8, 64
+    q, k, v = (to_device(a) for a in random_qkv(7700 + N, B, H, N, d))
+    scale = fp32_scale(d)
+    o1, l1 = fa.fa_fwd(q, k, v, scale=scale, causal=causal)
+    cfg = fa.launch_cfg(B, H, N, d, causal)
+    o2, l2 = fa.fa_fwd(q, k, v, scale=scale, causal=causal, cfg=cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
