@@ -16,7 +16,7 @@ from .buildlib import LIB, build  # noqa: F401
 __all__ = ["fa_fwd", "fa_fwd_ptr", "fa_fwd_cfg", "fa_fwd_ex", "fa_fwd_ex_ptr", "fa_fwd_splitkv",
            "splitkv_workspace_bytes", "splitkv_default_splits", "FwdDesc", "FaError", "strerror",
            "version", "default_cfg", "launch_cfg", "variants", "load_library", "EXPORTED_SYMBOLS", "fa_bwd", "fa_bwd_ptr",
-           "bwd_workspace_bytes", "fa_bwd_ex", "fa_bwd_ex_ptr", "BwdDesc"]
+           "bwd_workspace_bytes", "fa_bwd_ex", "fa_bwd_ex_ptr", "BwdDesc", "attention"]
 
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_cfg", "fa_fwd_ex", "fa_fwd_ex_cfg", "fa_fwd_splitkv",
                     "fa_splitkv_workspace_bytes", "fa_splitkv_default_splits", "fa_default_cfg", "fa_launch_cfg", "fa_num_variants",
@@ -451,3 +451,47 @@ def fa_bwd_ex(q, k, v, out, lse, dout, scale: float | None = None, causal: bool 
     desc.stream = _stream_handle(stream, q.device)
     _check(fa_bwd_ex_ptr(desc))
     return tuple(grads)
+
+
+_autograd_fn = None
+
+
+def _attention_function():
+    """The torch.autograd.Function over fa_fwd_ex / fa_bwd_ex (built on first use,
+    so that importing the package does not import torch)."""
+    global _autograd_fn
+    if _autograd_fn is None:
+        import torch
+
+        class FlashAttention(torch.autograd.Function):
+            """out = softmax(scale * q k^T) v on the library's kernels; the
+            backward recomputes P from the saved log-sum-exp."""
+
+            @staticmethod
+            def forward(ctx, q, k, v, causal, scale):
+                out, lse = fa_fwd_ex(q, k, v, scale=scale, causal=causal)
+                ctx.save_for_backward(q, k, v, out, lse)
+                ctx.causal, ctx.scale = causal, scale
+                return out
+
+            @staticmethod
+            def backward(ctx, dout):
+                q, k, v, out, lse = ctx.saved_tensors
+                dq, dk, dv = fa_bwd_ex(q, k, v, out, lse, dout.contiguous() if dout.stride(3) != 1 else dout,
+                                       scale=ctx.scale, causal=ctx.causal)
+                return dq, dk, dv, None, None
+
+        _autograd_fn = FlashAttention
+    return _autograd_fn
+
+
+def attention(q, k, v, causal: bool = False, scale: float | None = None):
+    """Differentiable attention on the library's kernels: ``q`` [B, H, Nq, d],
+    ``k, v`` [B, H, Nk, d] views (bf16 or fp16 for gradients; any strides with a
+    contiguous last dimension), causal masking top-left.  Returns ``out``; its
+    backward computes dq, dk, dv with ``fa_bwd_ex`` from the saved output and
+    log-sum-exp.  d is 64 or 128 when gradients are needed."""
+    import torch
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(q.shape[-1]), dtype=torch.float32))
+    return _attention_function().apply(q, k, v, bool(causal), float(scale))
