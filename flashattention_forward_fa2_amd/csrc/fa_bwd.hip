@@ -105,6 +105,24 @@ bool may_overlap(const Footprint& a, const Footprint& b) {
   return !(ab >= a.row_span && ba >= b.row_span);
 }
 
+// Every element of a strided [B, H, N, d] view has an address of its own: with
+// the dimensions ordered by stride, each stride is at least the span of all the
+// smaller ones (size-1 dimensions impose nothing).  Sufficient, and what a
+// written gradient needs so that no two lanes store to one element.
+bool self_disjoint(const long long st[3], int B, int H, int N, int d) {
+  long long dims[3][2] = {{st[0], B}, {st[1], H}, {st[2], N}};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (dims[j][0] < dims[i][0]) std::swap(dims[i], dims[j]);
+  long long span = d;
+  for (const auto& dm : dims) {
+    if (dm[1] == 1) continue;
+    if (dm[0] < span) return false;
+    span += dm[0] * (dm[1] - 1);
+  }
+  return true;
+}
+
 bool contiguous(const long long st[3], int H, int N, int d) {
   return st[2] == d && st[1] == (long long)N * d && st[0] == (long long)H * N * d;
 }
@@ -150,6 +168,9 @@ int validate(const fa_bwd_desc& a) {
     for (const auto& r : read)
       if (may_overlap(written[i], r)) return FA_ERR_ALIAS;
   }
+  if (!self_disjoint(a.dq_stride, a.B, a.H, a.N, a.d) || !self_disjoint(a.dk_stride, a.B, a.H, Nk, a.d) ||
+      !self_disjoint(a.dv_stride, a.B, a.H, Nk, a.d))
+    return FA_ERR_ALIAS;
   return FA_OK;
 }
 

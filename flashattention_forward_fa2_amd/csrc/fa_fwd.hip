@@ -199,6 +199,25 @@ bool strides_ok(const long long st[3], int N, int d, int elem = 2) {
   return st[2] >= d && (long long)(N + 256) * st[2] * elem < (1LL << 31);
 }
 
+// Every element of a strided [B, H, N, d] view has an address of its own: with
+// the dimensions ordered by stride, each stride is at least the span of all the
+// smaller ones (the contiguous head dimension spans d; size-1 dimensions impose
+// nothing).  Sufficient, and what a written tensor needs so that no two lanes
+// store to one element.
+bool self_disjoint(const long long st[3], int B, int H, int N, int d) {
+  long long dims[3][2] = {{st[0], B}, {st[1], H}, {st[2], N}};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (dims[j][0] < dims[i][0]) std::swap(dims[i], dims[j]);
+  long long span = d;
+  for (const auto& dm : dims) {
+    if (dm[1] == 1) continue;
+    if (dm[0] < span) return false;
+    span += dm[0] * (dm[1] - 1);
+  }
+  return true;
+}
+
 // Host-only checks of a descriptor, in a fixed order; no HIP call is made here.
 int validate_desc(const fa_fwd_desc& a) {
   if (!a.q || !a.k || !a.v || !a.out || !a.lse) return FA_ERR_NULL;
@@ -228,6 +247,8 @@ int validate_desc(const fa_fwd_desc& a) {
     if (overlaps(a.out, (size_t)ob, in.first, (size_t)in.second) || overlaps(a.lse, (size_t)lb, in.first, (size_t)in.second))
       return FA_ERR_ALIAS;
   if (overlaps(a.out, (size_t)ob, a.lse, (size_t)lb)) return FA_ERR_ALIAS;
+  const long long lst2[3] = {a.lse_stride[0], a.lse_stride[1], 1};
+  if (!self_disjoint(a.o_stride, a.B, a.H, a.Nq, a.d) || !self_disjoint(lst2, a.B, a.H, a.Nq, 1)) return FA_ERR_ALIAS;
   return FA_OK;
 }
 

@@ -94,9 +94,19 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
  * fa_bwd_workspace_bytes(B, H, N, d).
  * Errors, in this order: FA_ERR_NULL (desc or a pointer), FA_ERR_SHAPE (B, H,
  * N or Nk < 1, or B*H*max(N, Nk) >= 2^31), FA_ERR_HEAD_DIM, FA_ERR_STRIDE, FA_ERR_SCALE,
- * FA_ERR_ARG (causal, dtype), FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_ALIAS
- * (judged on each tensor's whole byte extent, as for fa_bwd), FA_ERR_NO_DEVICE,
- * FA_ERR_LAUNCH.  When every tensor is contiguous [B, H, N, d] (lse [B, H, N])
+ * FA_ERR_ARG (causal, dtype), FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_ALIAS,
+ * FA_ERR_NO_DEVICE, FA_ERR_LAUNCH.
+ * Aliasing (FA_ERR_ALIAS): dq, dk, dv and the workspace must not overlap one
+ * another or any input.  Two tensors overlap when their byte extents meet,
+ * unless both are views with one row stride rs, batch strides that are
+ * multiples of rs and all heads of a row within rs bytes, whose base addresses
+ * modulo rs start intervals (of the row's span) that do not meet: then their
+ * bytes are provably disjoint -- dq, dk, dv interleaved in one packed
+ * [B, N, 3, H, d] buffer, for instance.  And dq, dk, dv must not overlap
+ * themselves: with the dimensions ordered by stride, each stride at least the
+ * span of the smaller ones (size-1 dimensions aside).  So a zero head stride,
+ * e.g. for keys shared by several query heads, is refused for dk and dv: such
+ * gradients must be summed, which the caller does over per-head buffers.  When every tensor is contiguous [B, H, N, d] (lse [B, H, N])
  * the call runs the same kernels as fa_bwd, with identical results for bf16.
  */
 typedef struct fa_bwd_desc {

@@ -120,7 +120,10 @@ int fa_fwd_cfg(const void *q, const void *k, const void *v, void *out, float *ls
  * bound to bytes / 2.
  * Aliasing (FA_ERR_ALIAS) is judged on each tensor's whole byte extent: out
  * and lse must not overlap q, k, v or each other (inputs may overlap each
- * other, e.g. three views of one packed QKV tensor).
+ * other, e.g. three views of one packed QKV tensor, or k, v with head stride
+ * 0 shared by every query head); and out and lse must not overlap themselves
+ * (with its dimensions ordered by stride, each stride at least the span of the
+ * smaller ones, size-1 dimensions aside), so that no element is written twice.
  * Other arguments, ownership, asynchrony and determinism as for fa_fwd.
  */
 typedef struct fa_fwd_desc {

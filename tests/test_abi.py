@@ -420,3 +420,27 @@ def test_launch_cfg_needs_a_device(lib):
     c = fa.TileCfg()
     assert lib.fa_launch_cfg(4, 8, 4096, 64, 0, 0, ctypes.byref(c)) == 8
     assert lib.fa_launch_cfg(4, 8, 4096, 64, 0, 0, None) == 1
+
+
+def test_written_tensors_must_not_overlap_themselves(lib):
+    """A zero or too-small stride on a written tensor would have two lanes store
+    one element: refused with FA_ERR_ALIAS (inputs may still share rows)."""
+    d = desc(o_stride=(8192, 0, 64))                        # every head's output on one head
+    assert lib.fa_fwd_ex(ctypes.byref(d)) == 7
+    d = desc(o_stride=(8192, 64 * 32, 64))                  # heads 32 rows apart, 64 rows each
+    assert lib.fa_fwd_ex(ctypes.byref(d)) == 7
+    d = desc(lse_stride=(128, 32))                          # lse rows of 64 entries 32 apart
+    assert lib.fa_fwd_ex(ctypes.byref(d)) == 7
+    assert bwd_ex(lib, dk_stride=(8192, 0, 64)) == 7
+    assert bwd_ex(lib, dv_stride=(0, 4096, 64), B=2, workspace_bytes=8 * 2 * 2 * 64) == 7
+
+
+def test_shared_key_heads_are_valid_inputs(lib):
+    """k, v with head stride 0 (one key head for every query head, as in
+    multi-query attention) pass the checks; the call reaches the device check."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    d = desc(k_stride=(4096, 0, 64), v_stride=(4096, 0, 64))
+    assert lib.fa_fwd_ex(ctypes.byref(d)) == 8
+    assert bwd_ex(lib, k_stride=(4096, 0, 64), v_stride=(4096, 0, 64)) == 8
