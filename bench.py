@@ -204,6 +204,9 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     per_mode = {}
+    # Algorithmic HBM bytes of one call: Q, K, V read once, O and LSE written once.
+    esz = 4 if args.dtype == "f32" else 2
+    algo_bytes = esz * B * H * (2.0 * N * d + 2.0 * Nk * d) + 4.0 * B * H * N
     for c in modes:
         ms = np.array([a.elapsed_time(b) for a, b in ev[c]])
         avg = float(ms.mean())
@@ -213,7 +216,7 @@ def main():
             kernel_ms_min=round(float(ms.min()), 5), kernel_ms_max=round(float(ms.max()), 5),
             tflops=round(tf, 2),
             frac_of_peak=round(tf / peak, 4),
-            hbm_gbs=round((4.0 * B * H * N * d + 4.0 * B * H * Nk * d + 4.0 * B * H * N) / (avg * 1e-3) / 1e9, 1),
+            hbm_gbs=round(algo_bytes / (avg * 1e-3) / 1e9, 1),
             cfg=list(cfg if cfg else fa.launch_cfg(B, H, N, d, bool(c), args.dtype)))
     # Outside the timed region: each mode again with the caches flushed before
     # every launch (a 512 MiB write, more than L2 and the 256 MB Infinity Cache).
@@ -233,14 +236,23 @@ def main():
         del junk
     dom_c = max(modes, key=lambda c: per_mode["causal" if c else "noncausal"]["kernel_ms_avg"])
     dom = per_mode["causal" if dom_c else "noncausal"]
-    roofline = dict(bound="mfma", achieved=dom["tflops"], peak=peak, unit="TFLOP/s",
-                    frac=dom["frac_of_peak"],
-                    traffic=measured_traffic(B, H, N, d, dom_c) if not general else None,
-                    peak_note=("fp32 dense MFMA peak" if args.dtype == "f32"
-                               else "bf16 and fp16 dense MFMA share the 2.5 PFLOP/s peak"),
-                    kernel="fa_fwd_kernel d=%d causal=%d cfg=%s" % (d, dom_c, dom["cfg"]),
-                    flops_per_launch=flops(B, H, N, d, dom_c, Nk))
-    if not args.no_gemm:
+    kname = ("fa_fwd_splitkv (split + merge kernels, S=%d) d=%d causal=%d" % (args.splitkv, d, dom_c)
+             if args.splitkv else "fa_fwd_kernel d=%d causal=%d cfg=%s" % (d, dom_c, dom["cfg"]))
+    # The bound is whichever roof the algorithmic work reaches first: the
+    # FLOPs at the MFMA peak or the bytes at the HBM peak (one query row per
+    # head, as in decoding, is a stream over K and V).
+    if algo_bytes / (PEAK_HBM_GBS * 1e9) > flops(B, H, N, d, dom_c, Nk) / (peak * 1e12):
+        roofline = dict(bound="hbm", achieved=dom["hbm_gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
+                        frac=round(dom["hbm_gbs"] / PEAK_HBM_GBS, 4), traffic=None,
+                        kernel=kname, bytes_per_launch=algo_bytes)
+    else:
+        roofline = dict(bound="mfma", achieved=dom["tflops"], peak=peak, unit="TFLOP/s",
+                        frac=dom["frac_of_peak"],
+                        traffic=measured_traffic(B, H, N, d, dom_c) if not general else None,
+                        peak_note=("fp32 dense MFMA peak" if args.dtype == "f32"
+                                   else "bf16 and fp16 dense MFMA share the 2.5 PFLOP/s peak"),
+                        kernel=kname, flops_per_launch=flops(B, H, N, d, dom_c, Nk))
+    if not args.no_gemm and roofline["bound"] == "mfma":
         g = attainable_gemm(torch, dev)
         roofline["attainable_gemm_tflops"] = g
         roofline["frac_of_attainable"] = round(dom["tflops"] / g, 4)
@@ -353,6 +365,9 @@ def main_bwd(args):
     ms_per_step = wall * 1e3 / args.steps
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     per_mode = {}
+    # Algorithmic HBM bytes of one call: Q, K, V read once, O and LSE written once.
+    esz = 4 if args.dtype == "f32" else 2
+    algo_bytes = esz * B * H * (2.0 * N * d + 2.0 * Nk * d) + 4.0 * B * H * N
     for c in modes:
         ms = np.array([a.elapsed_time(b) for a, b in ev[c]])
         avg = float(ms.mean())
