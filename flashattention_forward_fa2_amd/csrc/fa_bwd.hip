@@ -53,7 +53,7 @@ int check_device() {
 
 int check_sizes(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (d != 32 && d != 64 && d != 128) return FA_ERR_HEAD_DIM;
   const long long elems = (long long)B * H * N * d;
   if ((long long)(N + 256) * d >= (1LL << 30) || elems >= (1LL << 31)) return FA_ERR_SHAPE;
   return FA_OK;
@@ -137,7 +137,7 @@ int validate(const fa_bwd_desc& a) {
   const int Nk = key_rows(a);
   if (a.B < 1 || a.H < 1 || a.N < 1 || Nk < 1) return FA_ERR_SHAPE;
   if ((long long)a.B * a.H * std::max(a.N, Nk) >= (1LL << 31)) return FA_ERR_SHAPE;
-  if (a.d != 64 && a.d != 128) return FA_ERR_HEAD_DIM;
+  if (a.d != 32 && a.d != 64 && a.d != 128) return FA_ERR_HEAD_DIM;
   // q, out, dout, dq: N rows per head; k, v, dk, dv: Nk rows.
   const long long* tq[4] = {a.q_stride, a.o_stride, a.do_stride, a.dq_stride};
   const long long* tk[4] = {a.k_stride, a.v_stride, a.dk_stride, a.dv_stride};
@@ -242,7 +242,9 @@ int run(const fa_bwd_desc& a) {
     strided = strided || !contiguous(t, a.H, p.Nk, a.d);
   const hipStream_t s = static_cast<hipStream_t>(a.stream);
   hipError_t e;
-  if (a.d == 64)
+  if (a.d == 32)
+    e = a.causal ? launch_dt<32, true>(p, a.dtype, strided, s) : launch_dt<32, false>(p, a.dtype, strided, s);
+  else if (a.d == 64)
     e = a.causal ? launch_dt<64, true>(p, a.dtype, strided, s) : launch_dt<64, false>(p, a.dtype, strided, s);
   else
     e = a.causal ? launch_dt<128, true>(p, a.dtype, strided, s) : launch_dt<128, false>(p, a.dtype, strided, s);

@@ -42,7 +42,9 @@ long long fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *               bfloat16 [B, H, N, d] and float32 [B, H, N].  Read only.
  *   dout        device pointer, bfloat16 [B, H, N, d]: d loss / d out.  Read only.
  *   dq, dk, dv  device pointers, bfloat16 [B, H, N, d].  Written; every element.
- *   B, H, N, d, scale, causal   as for fa_fwd.
+ *   B, H, N, scale, causal   as for fa_fwd; d is 32, 64 or 128 (the backward
+ *               holds a wavefront's dK and dV rows in registers, which d = 256
+ *               would overflow; FA_ERR_HEAD_DIM).
  *   workspace   device memory of at least fa_bwd_workspace_bytes(B, H, N, d)
  *               bytes, 256-byte aligned, owned by the caller; its contents on
  *               entry are ignored and on return are unspecified.  Calls that

@@ -260,13 +260,15 @@ def test_bwd_header_compiles_as_c99(tmp_path):
 def test_bwd_workspace_bytes(lib):
     assert fa.bwd_workspace_bytes(4, 8, 4096, 64) == 8 * 4 * 8 * 4096
     assert fa.bwd_workspace_bytes(1, 1, 1, 128) == 8
+    assert fa.bwd_workspace_bytes(2, 1, 5, 32) == 80
+    assert lib.fa_bwd_workspace_bytes(1, 1, 1, 256) == -3
     assert lib.fa_bwd_workspace_bytes(1, 1, 1, 96) == -3
     assert lib.fa_bwd_workspace_bytes(0, 1, 1, 64) == -2
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), 1), (dict(dout=0), 1), (dict(dv=0), 1), (dict(ws=0), 1), (dict(lse=0), 1),
-    (dict(B=0), 2), (dict(N=1 << 24, d=128), 2), (dict(d=32), 3),
+    (dict(B=0), 2), (dict(N=1 << 24, d=128), 2), (dict(d=256), 3), (dict(d=96), 3),
     (dict(scale=0.0), 4), (dict(scale=float("nan")), 4), (dict(causal=2), 5),
     (dict(dout=6 * FAKE + 8), 6), (dict(dk=8 * FAKE + 2), 6), (dict(lse=5 * FAKE + 1), 6),
     (dict(ws=WS + 64), 12), (dict(nbytes=8 * 2 * 64 - 1), 12),
@@ -325,7 +327,7 @@ def test_bwd_ex_null_descriptor(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dq=0), 1), (dict(workspace=0), 1),
-    (dict(N=0), 2), (dict(B=1 << 12, H=1 << 10, N=1 << 9), 2), (dict(d=256), 3), (dict(d=32), 3),
+    (dict(N=0), 2), (dict(B=1 << 12, H=1 << 10, N=1 << 9), 2), (dict(d=256), 3), (dict(d=16), 3),
     (dict(q_stride=(8192, 4096, 68)), 11),          # row stride not a multiple of 8 elements
     (dict(dv_stride=(8192, 4096, 56)), 11),         # row stride < d
     (dict(k_stride=(-8192, 4096, 64)), 11),

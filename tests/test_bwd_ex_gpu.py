@@ -45,7 +45,7 @@ def oracle_check(got, q, k, v, dout, scale, causal, dtype, label):
         compare_grad(g, r, label="%s %s" % (label, name), dtype=dtype)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [0, 1])
 @pytest.mark.parametrize("B,H,N", [(1, 2, 300), (2, 1, 77), (1, 1, 1000)])
 def test_f16_matches_oracle(B, H, N, d, causal):
@@ -62,7 +62,7 @@ def test_f16_matches_oracle(B, H, N, d, causal):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [0, 1])
 def test_bnhd_layout_matches_oracle(dtype, d, causal):
     """Every tensor in [B, N, H, d] memory, lse in a padded [B, H, N + 40] buffer."""

@@ -57,7 +57,7 @@ def check(seed, B, H, N, d, causal, heads=None):
         compare_grad(g, r, label="%s %s" % (label, name))
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [0, 1])
 @pytest.mark.parametrize("B,H,N", [(1, 2, 256), (2, 2, 300), (1, 3, 77), (1, 2, 1000)])
 def test_bwd_matches_oracle(B, H, N, d, causal):
@@ -69,7 +69,7 @@ def test_bwd_b1_h8_n1024(causal):
     check(9100 + causal, 1, 8, 1024, 64, causal)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 def test_single_token_head(d):
     """N = 1: P = 1, so dv = dout and dq = dk = 0 up to the rounding of dP - D."""
     q, k, v, dout = problem(9200 + d, 2, 2, 1, d)

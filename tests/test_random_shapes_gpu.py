@@ -79,7 +79,7 @@ def test_random_problem(i):
     o_ref, l_ref = oracle.attention_rows(q, k, v, scale, causal, dtype=dt)
     tol = dict(o_max=F16_MAX, o_mean=F16_MEAN) if dt == "f16" else {}
     compare(bits_of(out), lse.cpu().numpy(), o_ref, l_ref, label=label, dtype=dt, **tol)
-    if d not in (64, 128):
+    if d not in (32, 64, 128):
         return
     g = normal_bits(p["seed"] + 3, B * H * Nq * d, dtype=dt).reshape(B, H, Nq, d)
     tg = place(g, layout, dt)
