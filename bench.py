@@ -365,9 +365,6 @@ def main_bwd(args):
     ms_per_step = wall * 1e3 / args.steps
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     per_mode = {}
-    # Algorithmic HBM bytes of one call: Q, K, V read once, O and LSE written once.
-    esz = 4 if args.dtype == "f32" else 2
-    algo_bytes = esz * B * H * (2.0 * N * d + 2.0 * Nk * d) + 4.0 * B * H * N
     for c in modes:
         ms = np.array([a.elapsed_time(b) for a, b in ev[c]])
         avg = float(ms.mean())
