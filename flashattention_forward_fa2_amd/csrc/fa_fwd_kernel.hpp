@@ -426,6 +426,11 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           oacc[qb][db] = E::mfma(va[db][kk], p[qb][kk], oacc[qb][db]);
+    // The row sums are first needed by the next tile; without a use here the
+    // compiler sinks their adds past the barrier, where they issue back to back
+    // with no MFMA in flight.  Used here, they interleave with the O^T MFMAs.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) asm volatile("" ::"v"(l[qb]));
   };
 
   auto step = [&](int j, int stage) {
