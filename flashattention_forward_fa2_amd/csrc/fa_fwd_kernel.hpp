@@ -419,10 +419,12 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
         }
     }
     // ---- O^T += V_j^T P^T ------------------------------------------------------
+    // Key-step major: the products of P's first 16 keys can start as soon as
+    // those are packed, while the rest of P is still being computed.
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int kk = 0; kk < BK / 16; ++kk)
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           oacc[qb][db] = E::mfma(va[db][kk], p[qb][kk], oacc[qb][db]);
