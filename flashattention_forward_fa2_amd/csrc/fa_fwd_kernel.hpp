@@ -362,8 +362,7 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
                          __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
         va[db][kk] = __builtin_bit_cast(v8, w);
       }
-    // ---- mask, online softmax, P -> bf16 -------------------------------------
-    v8 p[QB][BK / 16];
+    // ---- mask, online softmax, P -> bf16, O^T += V_j^T P^T ----------------------
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       if (masked) {
@@ -394,40 +393,33 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
       const float m_sub = (m_new == -__builtin_inff()) ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m[qb] - m_sub);
       m[qb] = m_new;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < BK / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r], qk_scale, -m_sub));
-          s[qb][kb][r] = e;
-          rs += e;
-        }
-      l[qb] = fmaf(alpha, l[qb], rs);
       if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha;
       }
+      // P for 16 keys at a time (half of an S^T block: elements 8h .. 8h + 7),
+      // packed to the B operand and multiplied at once: the O^T += V^T P^T
+      // products of the first keys run while the later keys' P is computed.
+      // Row-sum and accumulation orders are the plain ones (keys ascending).
+      float rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < BK / 32; ++kb)
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int kb = kk >> 1, h = kk & 1;
+        float e8[8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          u32x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = E::pack(s[qb][kb][8 * h + 2 * e], s[qb][kb][8 * h + 2 * e + 1]);
-          p[qb][2 * kb + h] = __builtin_bit_cast(v8, w);
+        for (int i = 0; i < 8; ++i) {
+          e8[i] = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][8 * h + i], qk_scale, -m_sub));
+          rs += e8[i];
         }
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = E::pack(e8[2 * e], e8[2 * e + 1]);
+        const v8 pk = __builtin_bit_cast(v8, w);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[qb][db] = E::mfma(va[db][kk], pk, oacc[qb][db]);
+      }
+      l[qb] = fmaf(alpha, l[qb], rs);
     }
-    // ---- O^T += V_j^T P^T ------------------------------------------------------
-    // Key-step major: the products of P's first 16 keys can start as soon as
-    // those are packed, while the rest of P is still being computed.
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          oacc[qb][db] = E::mfma(va[db][kk], p[qb][kk], oacc[qb][db]);
     // The row sums are first needed by the next tile; without a use here the
     // compiler sinks their adds past the barrier, where they issue back to back
     // with no MFMA in flight.  Used here, they interleave with the O^T MFMAs.
