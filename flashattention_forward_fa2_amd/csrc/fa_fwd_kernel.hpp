@@ -365,6 +365,18 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
     // ---- mask, online softmax, P -> bf16, O^T += V_j^T P^T ----------------------
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+      // The lane's maximum is taken before the masked branch, in the block of
+      // the S^T MFMAs, so the first key block's maximum overlaps the second
+      // block's products; a masked tile (diagonal or ragged) takes it again.
+      auto lane_max = [&]() {
+        float x = fmaxf(s[qb][0][0], s[qb][0][1]);
+#pragma unroll
+        for (int kb = 0; kb < BK / 32; ++kb)
+#pragma unroll
+          for (int r = (kb == 0 ? 2 : 0); r < 16; ++r) x = fmaxf(x, s[qb][kb][r]);
+        return x;
+      };
+      float mx = lane_max();
       if (masked) {
         const int query = qw + qb * 32 + lr;
 #pragma unroll
@@ -374,12 +386,8 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
             const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
             if ((CAUSAL && key > query) || key >= klim) s[qb][kb][r] = -__builtin_inff();
           }
+        mx = lane_max();
       }
-      float mx = fmaxf(s[qb][0][0], s[qb][0][1]);
-#pragma unroll
-      for (int kb = 0; kb < BK / 32; ++kb)
-#pragma unroll
-        for (int r = (kb == 0 ? 2 : 0); r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
       mx = lane_swap_max(mx);
       // Lazy reference maximum: m moves only when the tile's maximum exceeds it
       // by more than kLazyMax (log2 units); until then P may reach 2^kLazyMax,
