@@ -81,6 +81,9 @@ def parse():
                     help="override the workload's head dimension (same B, H, N and distributions)")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward (fa_bwd: dQ, dK, dV from the forward's out and LSE) instead")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other workloads (4 and 5: the long-context targets; 1 and 2: the short ones)")
+    ap.add_argument("--extra-steps", type=int, default=10, help="timed launches per mode of workloads 4 and 5")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="instead of attention, run a plain device copy of MIB MiB (calibrates byte counters)")
     return ap.parse_args()
@@ -232,7 +235,11 @@ def main():
                 b.record(stream)
             torch.cuda.synchronize()
             fms = np.array([a.elapsed_time(b) for a, b in fev])
-            per_mode["causal" if c else "noncausal"]["kernel_ms_flushed_median"] = round(float(np.median(fms)), 5)
+            pm = per_mode["causal" if c else "noncausal"]
+            pm["kernel_ms_flushed_median"] = round(float(np.median(fms)), 5)
+            tf_fl = flops(B, H, N, d, c, Nk) / (float(np.median(fms)) * 1e-3) / 1e12
+            pm["tflops_flushed"] = round(tf_fl, 2)
+            pm["frac_of_peak_flushed"] = round(tf_fl / peak, 4)
         del junk
     dom_c = max(modes, key=lambda c: per_mode["causal" if c else "noncausal"]["kernel_ms_avg"])
     dom = per_mode["causal" if dom_c else "noncausal"]
@@ -280,7 +287,97 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if rec["vs_baseline"] is not None:
+        rec["vs_baseline_basis"] = ("the pages' final Triton kernel on this workload and step (RTX 4070 SUPER, "
+                                    "1.954 + 1.077 ms): another machine's figure, context only")
+    if cpu is not None:
+        rec["vs_cpu_baseline"] = round(value / cpu["value"], 1)
+    default_run = (args.workload == 3 and args.layout == "bhnd" and args.nq is None and args.splitkv is None
+                   and args.dtype == "bf16" and not args.headdim and not args.cfg and not args.only)
+    if default_run and not args.no_extra:
+        del q, k, v, outs, lses
+        torch.cuda.empty_cache()
+        rec["targets"] = {"B1-H32-N32768-d128 causal": other_workload(4, [1], args.extra_steps, 5, 8),
+                          "B4-H32-N8192-d128-peaked non-causal": other_workload(5, [0], args.extra_steps, 5, 8)}
+        rec["short_configs"] = {"B1-H1-N256-d64": other_workload(1, [0], 50, 20, None),
+                                "B1-H8-N1024-d64": other_workload(2, [0, 1], 50, 20, None)}
     print(json.dumps(rec), flush=True)
+
+
+def other_workload(wl, modes, steps, flush_reps, rows_per_head):
+    """One more workload through fa_fwd with the default launch: per mode, kernel
+    time from HIP events on the launch stream (back to back after a short ramp,
+    and again each launch after a 512 MiB cache flush), TFLOP/s and fraction of
+    the bf16 dense peak both ways, algorithmic HBM GB/s, and the output's parity
+    with the oracle on every row (rows_per_head None) or on a row sample."""
+    import torch
+    import flashattention_forward_fa2_amd as fa
+    import inputs
+    import oracle
+    from inputs import bits_to_f64, sample_rows, workload_seed
+
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS[wl]
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    scale = inputs.default_scale(d)
+    t0 = time.time()
+    q_bits, k_bits, v_bits = inputs.make_qkv(wl)
+    print("[bench] inputs %s generated in %.1fs" % (w["name"], time.time() - t0), file=sys.stderr, flush=True)
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    algo_bytes = 2.0 * B * H * 4 * N * d + 4.0 * B * H * N
+    res = {"B": B, "H": H, "N": N, "d": d, "sigma_qk": w["sigma_qk"]}
+    junk = torch.empty(512 << 18, dtype=torch.float32, device=dev)
+    for c in modes:
+        launch = lambda: fa.fa_fwd(q, k, v, scale=scale, causal=bool(c), out=out, lse=lse, stream=stream)
+        launch()
+        torch.cuda.synchronize()
+        t_end = time.time() + 0.3
+        while time.time() < t_end:
+            launch()
+            torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            launch()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in ev])
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(flush_reps)]
+        for a, b in fev:
+            junk.fill_(1.0)
+            a.record(stream)
+            launch()
+            b.record(stream)
+        torch.cuda.synchronize()
+        fms = np.array([a.elapsed_time(b) for a, b in fev])
+        f = flops(B, H, N, d, c)
+        avg, fmed = float(ms.mean()), float(np.median(fms))
+        entry = dict(kernel_ms_avg=round(avg, 5), kernel_ms_median=round(float(np.median(ms)), 5),
+                     kernel_ms_min=round(float(ms.min()), 5), kernel_ms_max=round(float(ms.max()), 5),
+                     tflops=round(f / (avg * 1e-3) / 1e12, 2), frac_of_peak=round(f / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     kernel_ms_flushed_median=round(fmed, 5),
+                     tflops_flushed=round(f / (fmed * 1e-3) / 1e12, 2),
+                     frac_of_peak_flushed=round(f / (fmed * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     hbm_gbs=round(algo_bytes / (avg * 1e-3) / 1e9, 1),
+                     hbm_gbs_flushed=round(algo_bytes / (fmed * 1e-3) / 1e9, 1),
+                     cfg=list(fa.launch_cfg(B, H, N, d, bool(c))), launches=steps, flushed_launches=flush_reps)
+        # parity of this output with the oracle
+        rows = (np.arange(B * H * N, dtype=np.int64) if rows_per_head is None
+                else sample_rows(workload_seed(wl, 3), B, H, N, per_head=rows_per_head))
+        o_ref, l_ref = oracle.attention_rows(q_bits, k_bits, v_bits, scale, bool(c), rows)
+        o = bits_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16)).reshape(-1, d)[rows]
+        L = lse.cpu().numpy().reshape(-1)[rows]
+        err = np.abs(o - o_ref)
+        entry["parity"] = dict(rows=int(rows.size), max_abs=float(err.max()), mean_abs=float(err.mean()),
+                               lse_rel=float((np.abs(L - l_ref) / np.maximum(1.0, np.abs(l_ref))).max()))
+        res["causal" if c else "noncausal"] = entry
+    del junk, q, k, v, out, lse
+    torch.cuda.empty_cache()
+    return res
 
 
 BWD_METRIC = "attention bwd TFLOP/s (bf16, dQ dK dV; 2.5x the forward's FLOPs) and % of bf16 MFMA peak"

@@ -134,9 +134,14 @@ __device__ __forceinline__ int lds_offset(int row, int chunk) {
   return row * (D * 2) + ((chunk ^ swz<D>(row)) << 4);
 }
 
+// Maximum of two scores.  The operands are MFMA results or -inf, never NaN,
+// so the IEEE maximum (no quieting of signalling NaNs needed, unlike fmaxf)
+// gives the same value and lowers to v_maximum3_f32 chains.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float lane_swap_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float lane_swap_sum(float x) {
@@ -369,23 +374,25 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
       // the S^T MFMAs, so the first key block's maximum overlaps the second
       // block's products; a masked tile (diagonal or ragged) takes it again.
       auto lane_max = [&]() {
-        float x = fmaxf(s[qb][0][0], s[qb][0][1]);
+        float x = vmax(s[qb][0][0], s[qb][0][1]);
 #pragma unroll
         for (int kb = 0; kb < BK / 32; ++kb)
 #pragma unroll
-          for (int r = (kb == 0 ? 2 : 0); r < 16; ++r) x = fmaxf(x, s[qb][kb][r]);
+          for (int r = (kb == 0 ? 2 : 0); r < 16; ++r) x = vmax(x, s[qb][kb][r]);
         return x;
       };
       float mx = lane_max();
       if (masked) {
-        const int query = qw + qb * 32 + lr;
+        // Element r of key block kb holds key k0 + 4g + o(kb, r) with the
+        // compile-time offset o = 32 kb + 8 (r / 4) + r % 4; it is masked when
+        // o >= lim (past the query causally, or past the last key).
+        const int base = k0 + 4 * g;
+        const int lim = CAUSAL ? min(qw + qb * 32 + lr + 1, klim) - base : klim - base;
 #pragma unroll
         for (int kb = 0; kb < BK / 32; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if ((CAUSAL && key > query) || key >= klim) s[qb][kb][r] = -__builtin_inff();
-          }
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[qb][kb][r] = -__builtin_inff();
         mx = lane_max();
       }
       mx = lane_swap_max(mx);
@@ -417,7 +424,7 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           e8[i] = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][8 * h + i], qk_scale, -m_sub));
-          rs += e8[i];
+          rs = (kk == 0 && i == 0) ? e8[i] : rs + e8[i];
         }
         u32x4 w;
 #pragma unroll
