@@ -305,11 +305,17 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
       }
   }
 
+  // m: the lazy reference maximum (log2 units of the scaled scores); thr =
+  // m + kLazyMax, the score above which m moves.  m starts at the lowest
+  // finite float instead of -inf, so exp2(s - m) and exp2(m_old - m_new) never
+  // see inf - inf: a row that has not met a visible key yet keeps it (its P are
+  // exp2(-inf) = 0), and the first finite score moves it with alpha = 0.
   f32x16 oacc[QB][D / 32];
-  float m[QB], l[QB];
+  float m[QB], thr[QB], l[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -__builtin_inff();
+    m[qb] = -__FLT_MAX__;
+    thr[qb] = -__FLT_MAX__;
     l[qb] = 0.f;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) oacc[qb][db] = f32x16{};
@@ -399,19 +405,20 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
       // Lazy reference maximum: m moves only when the tile's maximum exceeds it
       // by more than kLazyMax (log2 units); until then P may reach 2^kLazyMax,
       // far from fp32 / bf16 / fp16 overflow for P and O.  O / l and
-      // LSE = m + log2 l hold for any reference m, and most tiles then skip
-      // the O rescale.
+      // LSE = m + log2 l hold for any reference m, so most tiles skip the
+      // rescale of O and l, and alpha, altogether.
       const float mt = mx * qk_scale;
-      const float m_new = (mt > m[qb] + kLazyMax) ? mt : m[qb];
-      // A row that has seen no visible key yet keeps m = -inf; subtract 0 then
-      // so that exp2(-inf - (-inf)) never appears.
-      const float m_sub = (m_new == -__builtin_inff()) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m[qb] - m_sub);
-      m[qb] = m_new;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+      const bool moves = mt > thr[qb];
+      if (__builtin_amdgcn_ballot_w64(moves)) {
+        const float m_new = moves ? mt : m[qb];
+        const float alpha = __builtin_amdgcn_exp2f(m[qb] - m_new);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha;
+        l[qb] *= alpha;
+        m[qb] = m_new;
+        thr[qb] = m_new + kLazyMax;
       }
+      const float m_sub = m[qb];
       // P for 16 keys at a time (half of an S^T block: elements 8h .. 8h + 7),
       // packed to the B operand and multiplied at once: the O^T += V^T P^T
       // products of the first keys run while the later keys' P is computed.
@@ -433,7 +440,7 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) oacc[qb][db] = E::mfma(va[db][kk], pk, oacc[qb][db]);
       }
-      l[qb] = fmaf(alpha, l[qb], rs);
+      l[qb] += rs;
     }
     // The row sums are first needed by the next tile; without a use here the
     // compiler sinks their adds past the barrier, where they issue back to back
