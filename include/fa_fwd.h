@@ -55,7 +55,9 @@ enum fa_status {
  *   lse      device pointer, float32, contiguous [B, H, N]: the natural-log
  *            log-sum-exp of each query row's scaled scores.  Written.
  *   B, H, N  batch, heads, sequence length (>= 1); B*H*N*d must stay below
- *            2^31 elements per tensor and N*d below 2^31.
+ *            2^31 elements per tensor and (N + 256)*d below 2^30, so that one
+ *            head's bytes stay within the 32-bit offsets of a buffer resource
+ *            (else FA_ERR_SHAPE).
  *   d        head dimension: 32, 64, 128 or 256.
  *   scale    softmax scale applied to q.k (typically 1/sqrt(d)); finite, > 0
  *            (the running maximum is kept in scaled units, which needs scale > 0).

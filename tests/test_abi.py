@@ -80,6 +80,17 @@ def test_argument_errors_return_codes(lib, kw, code):
     assert call(**kw) == code
 
 
+def test_head_extent_limit_edge(lib):
+    """(N + 256) * d must stay below 2^30 (one head's bytes within the 32-bit
+    offsets of a buffer resource): the first N that reaches it is refused, the
+    one below passes every host check (and stops at the device check on a host
+    without a gfx950).  The tensors are 2 GiB apart, so they do not overlap."""
+    d, far = 64, 1 << 32
+    N = (1 << 30) // d - 256
+    assert call(N=N, d=d, q=far, k=2 * far, v=3 * far, out=4 * far, lse=5 * far) == 2
+    assert call(N=N - 1, d=d, q=far, k=2 * far, v=3 * far, out=4 * far, lse=5 * far) in (0, 8)
+
+
 def test_inputs_may_alias_each_other(lib):
     # q = k = v is a legal self-attention call: it passes validation (and then
     # stops at the device check on a host without a gfx950).
