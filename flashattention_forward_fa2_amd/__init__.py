@@ -16,16 +16,18 @@ from .buildlib import LIB, build  # noqa: F401
 __all__ = ["fa_fwd", "fa_fwd_ptr", "fa_fwd_cfg", "fa_fwd_ex", "fa_fwd_ex_ptr", "fa_fwd_splitkv",
            "splitkv_workspace_bytes", "splitkv_default_splits", "FwdDesc", "FaError", "strerror",
            "version", "default_cfg", "launch_cfg", "variants", "load_library", "EXPORTED_SYMBOLS", "fa_bwd", "fa_bwd_ptr",
-           "bwd_workspace_bytes", "fa_bwd_ex", "fa_bwd_ex_ptr", "BwdDesc", "attention"]
+           "bwd_workspace_bytes", "fa_bwd_ex", "fa_bwd_ex_ptr", "BwdDesc", "attention", "fa_fwd_splitkv_noalloc",
+           "SPLITKV_NOALLOC_MAX_BYTES"]
 
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_cfg", "fa_fwd_ex", "fa_fwd_ex_cfg", "fa_fwd_splitkv",
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_cfg", "fa_fwd_ex", "fa_fwd_ex_cfg", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc",
                     "fa_splitkv_workspace_bytes", "fa_splitkv_default_splits", "fa_default_cfg", "fa_launch_cfg", "fa_num_variants",
                     "fa_variant", "fa_variant_dtype", "fa_strerror", "fa_version", "fa_bwd", "fa_bwd_ex",
                     "fa_bwd_workspace_bytes")
 
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD_DIM", 4: "FA_ERR_SCALE",
           5: "FA_ERR_ARG", 6: "FA_ERR_ALIGN", 7: "FA_ERR_ALIAS", 8: "FA_ERR_NO_DEVICE",
-          9: "FA_ERR_LAUNCH", 10: "FA_ERR_INTERNAL", 11: "FA_ERR_STRIDE", 12: "FA_ERR_WORKSPACE"}
+          9: "FA_ERR_LAUNCH", 10: "FA_ERR_INTERNAL", 11: "FA_ERR_STRIDE", 12: "FA_ERR_WORKSPACE",
+          13: "FA_ERR_SCRATCH"}
 
 
 class FaError(RuntimeError):
@@ -112,6 +114,8 @@ def load_library():
             lib.fa_fwd_ex_cfg.restype = _I
             lib.fa_fwd_splitkv.argtypes = [ctypes.POINTER(FwdDesc), _I, _P, ctypes.c_longlong]
             lib.fa_fwd_splitkv.restype = _I
+            lib.fa_fwd_splitkv_noalloc.argtypes = [ctypes.POINTER(FwdDesc), _I]
+            lib.fa_fwd_splitkv_noalloc.restype = _I
             lib.fa_splitkv_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
             lib.fa_splitkv_workspace_bytes.restype = ctypes.c_longlong
             lib.fa_splitkv_default_splits.argtypes = [_I, _I, _I, _I, _I, _I]
@@ -333,6 +337,20 @@ def fa_fwd_splitkv(q, k, v, scale: float | None = None, causal: bool = False, ou
     nbytes = workspace.numel() * workspace.element_size()
     _check(int(load_library().fa_fwd_splitkv(ctypes.byref(desc), int(num_splits), _P(workspace.data_ptr()),
                                              ctypes.c_longlong(nbytes))))
+    return out, lse
+
+
+# Bytes of the library's static split-key scratch (FA_SPLITKV_NOALLOC_MAX_BYTES).
+SPLITKV_NOALLOC_MAX_BYTES = 32 << 20
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse=None,
+                           stream=None, num_splits: int = 0):
+    """``fa_fwd_splitkv`` with its partial results in the library's static
+    per-GPU scratch instead of a workspace (nothing is allocated for them).
+    Returns ``(out, lse)``; raises FA_ERR_SCRATCH when they would not fit."""
+    desc, out, lse = _make_desc(q, k, v, scale, causal, out, lse, stream)
+    _check(int(load_library().fa_fwd_splitkv_noalloc(ctypes.byref(desc), int(num_splits))))
     return out, lse
 
 

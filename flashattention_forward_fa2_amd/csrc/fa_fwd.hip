@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kVersion = 400;  // 0.4.0
+constexpr int kVersion = 500;  // 0.5.0
 
 using Launcher = hipError_t (*)(const fa::Params&, int B, hipStream_t);
 
@@ -363,6 +363,47 @@ int run_splitkv(const fa_fwd_desc& a, int num_splits, void* ws, long long ws_byt
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// ---- key splits without an allocation ---------------------------------------------
+// The partial results of fa_fwd_splitkv_noalloc live in this file-scope device
+// array instead of a caller's workspace: every GPU the library runs on holds
+// one copy until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it is only a stand-in for the device symbol); it
+// uses the device address hipGetSymbolAddress returns, looked up once per
+// device with that device current.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[FA_SPLITKV_NOALLOC_MAX_BYTES];
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+// FA_OK with *ptr = this device's copy of `scratch`, or an error code.
+int scratch_address(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_NO_DEVICE;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_ptr[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess ? p : nullptr;
+  });
+  if (!g_scratch_ptr[dev]) return FA_ERR_INTERNAL;
+  *ptr = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+int run_splitkv_noalloc(const fa_fwd_desc& a, int num_splits) {
+  const int st = validate_desc(a);
+  if (st != FA_OK) return st;
+  if (a.dtype == FA_DTYPE_F32) return FA_ERR_ARG;
+  if (num_splits < 0 || num_splits > 1024) return FA_ERR_ARG;
+  const int S = num_splits ? num_splits : default_splits(a.B, a.H, a.Nq, a.Nk, a.d);
+  if (split_workspace(a.B, a.H, a.Nq, a.d, split_count(a.Nk, S)) > FA_SPLITKV_NOALLOC_MAX_BYTES)
+    return FA_ERR_SCRATCH;
+  const int dst = check_device();
+  if (dst != FA_OK) return dst;
+  void* ws = nullptr;
+  const int sst = scratch_address(&ws);
+  if (sst != FA_OK) return sst;
+  return run_splitkv(a, num_splits, ws, FA_SPLITKV_NOALLOC_MAX_BYTES);
+}
+
 // The square, contiguous call as a descriptor.
 fa_fwd_desc square_desc(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int N,
                         int d, float scale, int causal, void* stream) {
@@ -449,6 +490,15 @@ int fa_fwd_splitkv(const fa_fwd_desc* desc, int num_splits, void* workspace, lon
   }
 }
 
+int fa_fwd_splitkv_noalloc(const fa_fwd_desc* desc, int num_splits) {
+  if (!desc) return FA_ERR_NULL;
+  try {
+    return run_splitkv_noalloc(*desc, num_splits);
+  } catch (...) {
+    return FA_ERR_INTERNAL;
+  }
+}
+
 int fa_launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, fa_tile_cfg* cfg) {
   if (!cfg) return FA_ERR_NULL;
   if (B < 1 || H < 1 || Nq < 1) return FA_ERR_SHAPE;
@@ -505,6 +555,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_INTERNAL: return "internal error";
     case FA_ERR_WORKSPACE: return "workspace missing, not 256-byte aligned or smaller than fa_splitkv_workspace_bytes";
     case FA_ERR_STRIDE: return "a stride is negative, not a multiple of 8 elements, shorter than a row, or too large";
+    case FA_ERR_SCRATCH: return "the split-key partial results exceed the static scratch (FA_SPLITKV_NOALLOC_MAX_BYTES)";
     default: return "unknown status";
   }
 }

@@ -43,7 +43,9 @@ enum fa_status {
   FA_ERR_INTERNAL = 10,  /* anything else (no C++ exception crosses this ABI)     */
   FA_ERR_STRIDE = 11,    /* a stride is negative, misaligned, smaller than a row, or
                             puts a head beyond the 32-bit addressing of one head  */
-  FA_ERR_WORKSPACE = 12  /* split-key workspace missing, misaligned or too small   */
+  FA_ERR_WORKSPACE = 12, /* split-key workspace missing, misaligned or too small   */
+  FA_ERR_SCRATCH = 13    /* fa_fwd_splitkv_noalloc: the partial results need more
+                            than FA_SPLITKV_NOALLOC_MAX_BYTES                     */
 };
 
 /*
@@ -172,6 +174,26 @@ int fa_fwd_ex_cfg(const fa_fwd_desc *desc, const fa_tile_cfg *cfg);
  * outside 0..1024.  Two kernels are enqueued on desc->stream.
  */
 int fa_fwd_splitkv(const fa_fwd_desc *desc, int num_splits, void *workspace, long long workspace_bytes);
+
+/*
+ * fa_fwd_splitkv without an allocation, for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same operation, arguments (minus
+ * the workspace), kernels and results as fa_fwd_splitkv; the partial results
+ * go to a static device array inside the library instead, one per GPU, held
+ * from the first call on that GPU until the process ends.  Up to
+ * FA_SPLITKV_NOALLOC_MAX_BYTES of it is used: a call whose
+ * fa_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits) exceeds that returns
+ * FA_ERR_SCRATCH and launches nothing.  The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); the first call on a GPU
+ * looks up the array's device address.  Every call on one GPU shares that
+ * GPU's array: two calls that may run at the same time on one GPU (different
+ * streams, or different host threads) race and give undefined results; calls
+ * ordered on one stream do not.  Nothing in the array needs to start at zero
+ * (every partial result the merge reads is written by the same call).
+ */
+#define FA_SPLITKV_NOALLOC_MAX_BYTES (32LL << 20)
+int fa_fwd_splitkv_noalloc(const fa_fwd_desc *desc, int num_splits);
 
 /* Workspace bytes for fa_fwd_splitkv (>= 0), or minus an error code. */
 long long fa_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);

@@ -252,6 +252,27 @@ def test_splitkv_valid_call_reaches_the_device_check(lib):
     assert lib.fa_fwd_splitkv(ctypes.byref(d), 0, ctypes.c_void_p(WS), ctypes.c_longlong(1 << 30)) == 8
 
 
+def test_splitkv_noalloc_host_checks(lib):
+    """The static-scratch entry point: NULL descriptor, the descriptor checks,
+    FA_ERR_SCRATCH (13) when the partial results exceed the scratch, decided on
+    the host before any device call, and the header's limit equals the
+    binding's."""
+    assert lib.fa_fwd_splitkv_noalloc(None, 0) == 1
+    assert lib.fa_fwd_splitkv_noalloc(ctypes.byref(desc(d=96)), 0) == 3
+    assert lib.fa_fwd_splitkv_noalloc(ctypes.byref(desc()), 2000) == 5
+    assert lib.fa_fwd_splitkv_noalloc(ctypes.byref(desc(dtype=2)), 2) == 5
+    far = 1 << 32  # tensors of 268 MB: keep the fake pointers apart
+    big = desc(B=4, H=32, Nq=512, Nk=8192, d=128, q=far, k=2 * far, v=3 * far, out=4 * far, lse=5 * far)
+    assert fa.splitkv_workspace_bytes(4, 32, 512, 8192, 128, 8) > fa.SPLITKV_NOALLOC_MAX_BYTES
+    assert lib.fa_fwd_splitkv_noalloc(ctypes.byref(big), 8) == 13
+    text = open(HEADERS[0]).read()
+    m = re.search(r"#define FA_SPLITKV_NOALLOC_MAX_BYTES \((\d+)LL << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.SPLITKV_NOALLOC_MAX_BYTES
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        assert lib.fa_fwd_splitkv_noalloc(ctypes.byref(desc(Nq=1, Nk=4096)), 0) == 8
+
+
 # ---------------------------------------------------------------- backward
 
 def bwd_call(**kw):
