@@ -71,6 +71,9 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLazyMax = 8.0f;  // see the online-softmax update in fa_fwd_kernel
 constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
+#ifndef FA_CAUSAL_GROUP
+#define FA_CAUSAL_GROUP 2  // heads per causal launch-order group on one XCD
+#endif
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b);
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b);
@@ -224,8 +227,12 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
   // ---- which (head, query tile) this workgroup owns -------------------------
   // Workgroups are dispatched round-robin over the 8 XCDs; when the head count
   // allows, ids are remapped so that each XCD works through a contiguous set of
-  // heads (their K/V stay in that XCD's L2).  Causal tiles run longest first,
-  // all heads' longest tiles before any shorter one.
+  // heads (their K/V stay in that XCD's L2).  Causal tiles run longest first
+  // within groups of FA_CAUSAL_GROUP heads of an XCD, one group after the
+  // other: a group's lengths n, n, n-1, n-1, ... and the next group's in the
+  // same order fill the compute units evenly (a unit freed by a tile of length
+  // i takes the next of length n + 1 - i), while only one group's K/V are live
+  // at the start of the group.
   const int split = SPLIT ? (int)(blockIdx.x % pr.nsplit) : 0;
   const int total = SPLIT ? (int)(gridDim.x / pr.nsplit) : (int)gridDim.x;
   const int i = SPLIT ? (int)(blockIdx.x / pr.nsplit) : (int)blockIdx.x;
@@ -236,8 +243,10 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
     if (xcd) {
       const int per = total >> 3, hpx = BH >> 3;
       const int chunk = t / per, j = t - chunk * per;
-      bh = chunk * hpx + j % hpx;
-      qt = nqt - 1 - j / hpx;
+      const int gs = (hpx % FA_CAUSAL_GROUP) == 0 ? FA_CAUSAL_GROUP : hpx;
+      const int grp = j / (gs * nqt), r = j - grp * gs * nqt;
+      bh = chunk * hpx + grp * gs + r % gs;
+      qt = nqt - 1 - r / gs;
     } else {
       bh = t % BH;
       qt = nqt - 1 - t / BH;
