@@ -175,12 +175,20 @@ int check_device(int* cus = nullptr) {
 }
 
 // The tile a launch uses when the caller names none: default_cfg_dt, except
-// that an 8-wavefront grid smaller than the GPU (B*H*ceil(Nq/256) workgroups,
-// one per CU at a time) takes 4-wavefront tiles, which doubles its workgroups.
+// on grids smaller than the GPU.  An 8-wavefront grid (B*H*ceil(Nq/256)
+// workgroups, one per CU at a time) with fewer workgroups than compute units
+// takes 4-wavefront tiles, which doubles its workgroups; at d = 64 and 128 a
+// 4-wavefront grid that still leaves compute units idle takes one-wavefront
+// tiles (32 queries per workgroup, four times the workgroups again; 32-key
+// tiles at d = 128).
 fa_tile_cfg launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, int cus) {
   fa_tile_cfg c = default_cfg_dt(Nq, d, causal, dtype);
-  const long long wgs = (long long)B * H * ((Nq + c.qb * c.waves * 32 - 1) / (c.qb * c.waves * 32));
-  if (c.waves == 8 && wgs < cus) c = fa_tile_cfg{1, 4, 64};
+  auto wgs = [&](const fa_tile_cfg& t) {
+    return (long long)B * H * ((Nq + t.qb * t.waves * 32 - 1) / (t.qb * t.waves * 32));
+  };
+  if (c.waves == 8 && wgs(c) < cus) c = fa_tile_cfg{1, 4, 64};
+  const fa_tile_cfg one{1, 1, d == 128 ? 32 : 64};
+  if ((d == 64 || d == 128) && c.waves == 4 && wgs(c) < cus && find_variant(d, causal, one, dtype)) c = one;
   return c;
 }
 

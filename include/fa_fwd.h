@@ -210,7 +210,9 @@ int fa_default_cfg(int N, int d, int causal, fa_tile_cfg *cfg);
 /* The configuration fa_fwd and fa_fwd_ex pick for these sizes and element type
  * on the current device: fa_default_cfg's, except that when its 8-wavefront
  * grid (B*H*ceil(Nq/256) workgroups) is smaller than the device's compute-unit
- * count, the 4-wavefront tile (1, 4, 64), which doubles the workgroups.
+ * count, the 4-wavefront tile (1, 4, 64), which doubles the workgroups, and at
+ * d = 64 or 128 (bf16 or fp16), when that grid too is smaller, the
+ * one-wavefront tile (1, 1, 64), or (1, 1, 32) at d = 128.
  * FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_ARG (causal, dtype)
  * or FA_ERR_NO_DEVICE. */
 int fa_launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, fa_tile_cfg *cfg);

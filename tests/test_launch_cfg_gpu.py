@@ -1,6 +1,7 @@
 """The tile fa_fwd picks on its own (fa_launch_cfg): 8-wavefront tiles when the
-grid fills the GPU, 4-wavefront tiles when it would not, and the default launch
-is bit-identical to the explicit launch of the configuration it names."""
+grid fills the GPU, 4-wavefront tiles when it would not, one-wavefront tiles at
+d = 64 and 128 when even those would not, and the default launch is bit-identical to the
+explicit launch of the configuration it names."""
 import numpy as np
 import pytest
 
@@ -25,8 +26,12 @@ def test_choice_follows_the_grid():
     import flashattention_forward_fa2_amd as fa
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     assert fa.launch_cfg(4, 8, 4096, 64, False) == (1, 8, 64)          # 512 workgroups of 256 queries
-    assert fa.launch_cfg(1, 8, 1024, 64, True) == (1, 4, 64)           # 32 of them: fewer than the CUs
-    assert fa.launch_cfg(1, 8, 1024, 128, False, "f16") == (1, 4, 64)
+    assert fa.launch_cfg(1, 8, 4096, 64, False) == (1, 4, 64)          # 128 of them; 256 of 128 queries
+    assert fa.launch_cfg(1, 8, 1024, 64, True) == (1, 1, 64)           # 32, then 64: fewer than the CUs
+    assert fa.launch_cfg(1, 8, 1024, 64, False, "f16") == (1, 1, 64)
+    assert fa.launch_cfg(1, 1, 256, 64, False) == (1, 1, 64)
+    assert fa.launch_cfg(1, 8, 1024, 128, False, "f16") == (1, 1, 32)  # d = 128: 32-key one-wave tiles
+    assert fa.launch_cfg(1, 8, 4096, 128, True) == (1, 4, 64)
     assert fa.launch_cfg(1, 8, 1024, 256, False) == (1, 4, 32)         # d = 256 has the 4-wave tile only
     assert fa.launch_cfg(1, 8, 1024, 64, False, "f32") == (1, 4, 32)
     n = 256 * ((cus + 7) // 8)                                         # 8 heads x n/256 tiles >= cus
@@ -34,11 +39,12 @@ def test_choice_follows_the_grid():
     assert fa.launch_cfg(1, 8, n - 256, 64, False) == (1, 4, 64)      # 8 * (ceil(cus / 8) - 1) < cus
 
 
-@pytest.mark.parametrize("N,causal", [(1024, True), (1024, False), (4096, False)])
+@pytest.mark.parametrize("N,causal", [(1024, True), (1024, False), (4096, False), (300, True)])
 def test_default_launch_equals_the_named_configuration(N, causal):
     import torch
     import flashattention_forward_fa2_amd as fa
-    B, H, d = 1, 8, 64
+    B, H = 1, 8
+    d = 128 if N == 300 else 64
     q, k, v = (to_device(a) for a in random_qkv(7700 + N, B, H, N, d))
     scale = fp32_scale(d)
     o1, l1 = fa.fa_fwd(q, k, v, scale=scale, causal=causal)
