@@ -297,14 +297,16 @@ def main():
     if default_run and not args.no_extra:
         del q, k, v, outs, lses
         torch.cuda.empty_cache()
-        rec["targets"] = {"B1-H32-N32768-d128 causal": other_workload(4, [1], args.extra_steps, 5, 8),
-                          "B4-H32-N8192-d128-peaked non-causal": other_workload(5, [0], args.extra_steps, 5, 8)}
-        rec["short_configs"] = {"B1-H1-N256-d64": other_workload(1, [0], 50, 20, None),
-                                "B1-H8-N1024-d64": other_workload(2, [0, 1], 50, 20, None)}
+        ramp = min(0.3, args.ramp_seconds)
+        fl = 5 if args.flush_reps > 0 else 0
+        rec["targets"] = {"B1-H32-N32768-d128 causal": other_workload(4, [1], args.extra_steps, fl, 8, ramp),
+                          "B4-H32-N8192-d128-peaked non-causal": other_workload(5, [0], args.extra_steps, fl, 8, ramp)}
+        rec["short_configs"] = {"B1-H1-N256-d64": other_workload(1, [0], 50, 4 * fl, None, ramp),
+                                "B1-H8-N1024-d64": other_workload(2, [0, 1], 50, 4 * fl, None, ramp)}
     print(json.dumps(rec), flush=True)
 
 
-def other_workload(wl, modes, steps, flush_reps, rows_per_head):
+def other_workload(wl, modes, steps, flush_reps, rows_per_head, ramp_seconds=0.3):
     """One more workload through fa_fwd with the default launch: per mode, kernel
     time from HIP events on the launch stream (back to back after a short ramp,
     and again each launch after a 512 MiB cache flush), TFLOP/s and fraction of
@@ -335,7 +337,7 @@ def other_workload(wl, modes, steps, flush_reps, rows_per_head):
         launch = lambda: fa.fa_fwd(q, k, v, scale=scale, causal=bool(c), out=out, lse=lse, stream=stream)
         launch()
         torch.cuda.synchronize()
-        t_end = time.time() + 0.3
+        t_end = time.time() + ramp_seconds
         while time.time() < t_end:
             launch()
             torch.cuda.synchronize()
@@ -353,7 +355,7 @@ def other_workload(wl, modes, steps, flush_reps, rows_per_head):
             launch()
             b.record(stream)
         torch.cuda.synchronize()
-        fms = np.array([a.elapsed_time(b) for a, b in fev])
+        fms = np.array([a.elapsed_time(b) for a, b in fev]) if fev else ms
         f = flops(B, H, N, d, c)
         avg, fmed = float(ms.mean()), float(np.median(fms))
         entry = dict(kernel_ms_avg=round(avg, 5), kernel_ms_median=round(float(np.median(ms)), 5),
