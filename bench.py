@@ -544,7 +544,7 @@ def measured_traffic(B, H, N, d, causal):
     (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's counts), or None when
     there is none for this shape or the kernel sources changed since."""
     from flashattention_forward_fa2_amd.buildlib import source_digest
-    path = os.path.join(ROOT, "profiles", "fa_fwd_d%d_B%dH%dN%d_hbm_traffic.md" % (d, B, H, N))
+    path = os.path.join(ROOT, "profiles", "fa_fwd_all_workloads_hbm_traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
