@@ -508,7 +508,7 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None):
     ``k, v`` [B, H, Nk, d] views (bf16 or fp16 for gradients; any strides with a
     contiguous last dimension), causal masking top-left.  Returns ``out``; its
     backward computes dq, dk, dv with ``fa_bwd_ex`` from the saved output and
-    log-sum-exp.  d is 64 or 128 when gradients are needed."""
+    log-sum-exp.  d is 32, 64 or 128 when gradients are needed."""
     import torch
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(q.shape[-1]), dtype=torch.float32))

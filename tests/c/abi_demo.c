@@ -99,11 +99,14 @@ int main(void) {
     CHECK(hipMemcpy(ho, o, n * 2, hipMemcpyDeviceToHost));
     CHECK(hipMemcpy(hl, l, (size_t)B * H * N * 4, hipMemcpyDeviceToHost));
     if (oracle_attention_rows(hq, hk, hv, B, H, N, d, scale, causal, rows, (int64_t)B * H * N, ro, rl) != 0) return 5;
+    double sum = 0.0;
     for (size_t i = 0; i < n; ++i) {
       const double e = fabs(from_bf16(ho[i]) - ro[i]);
       if (!(e <= 2e-2)) return 6;
       if (e > worst) worst = e;
+      sum += e;
     }
+    if (!(sum / (double)n <= 2e-3)) return 8;  /* mean absolute error bound */
     for (int64_t r = 0; r < (int64_t)B * H * N; ++r)
       if (!(fabs(hl[r] - rl[r]) <= 1e-4 * fmax(1.0, fabs(rl[r])))) return 7;
   }

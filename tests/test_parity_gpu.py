@@ -182,9 +182,37 @@ def test_errors_do_not_launch():
 
 @pytest.mark.parametrize("N,d,causal", [(1 << 19, 64, 1), ((1 << 20) + 17, 128, 0)])
 def test_very_long_single_head(N, d, causal):
-    """One head of half a million / a million keys: byte offsets inside a head
-    approach the 32-bit range the kernels use (N * d * 2 up to 2^28), and the
-    last tile is ragged.  Sampled rows, including the last ones."""
+    """One head of half a million / a million keys, the last tile ragged: byte
+    offsets inside a head reach N * d * 2 = 2^28, an eighth of the 2^31-byte
+    range of a head's buffer (test_head_near_the_byte_limit covers the rest).
+    Sampled rows, including the last ones."""
     q, k, v = random_qkv(7700 + d, 1, 1, N, d)
     rows = np.array([0, 1, 63, 64, 4095, N // 2, N - 65, N - 2, N - 1], dtype=np.int64)
     check_rows(q, k, v, fp32_scale(d), causal, rows=rows, label="long N=%d d=%d causal=%d" % (N, d, causal))
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_head_near_the_byte_limit(causal):
+    """Rows strided so that one head spans just under 2^31 bytes, the most the
+    host check admits ((N + 256) * row stride * 2 < 2^31): q, k, v and out of
+    2 GB each through fa_fwd_ex, the last tile ragged.  The kernels' 32-bit
+    byte offsets reach 2.02e9.  Sampled rows, including the last ones."""
+    import torch
+    import flashattention_forward_fa2_amd as fa
+    N, d = 4096 + 17, 64
+    rs = ((1 << 30) // (N + 256)) // 8 * 8          # elements per row
+    assert (N + 256) * rs * 2 < (1 << 31) <= (N + 256 + 8) * rs * 2
+    q, k, v = random_qkv(7900 + causal, 1, 1, N, d)
+    def strided(bits):
+        buf = torch.zeros(N * rs, dtype=torch.bfloat16, device="cuda:0")
+        t = buf.as_strided((1, 1, N, d), (N * rs, N * rs, rs, 1))
+        if bits is not None:
+            t.copy_(to_device(bits))
+        return t
+    tq, tk, tv, to = strided(q), strided(k), strided(v), strided(None)
+    out, lse = fa.fa_fwd_ex(tq, tk, tv, scale=fp32_scale(d), causal=bool(causal), out=to)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 63, 64, 2047, 4095, 4096, N - 17, N - 2, N - 1], dtype=np.int64)
+    o_bits = out.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    o_ref, l_ref = oracle.attention_rows(q, k, v, fp32_scale(d), causal, rows)
+    compare(o_bits, lse.cpu().numpy(), o_ref, l_ref, rows=rows, label="2 GB head causal=%d" % causal)
