@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kVersion = 500;  // 0.5.0
+constexpr int kVersion = 501;  // 0.5.1
 
 using Launcher = hipError_t (*)(const fa::Params&, int B, hipStream_t);
 
@@ -99,6 +99,9 @@ const Variant kVariants[] = {
     FA_VARIANTS_SMALL(FA_VARIANT16, 64, 0), FA_VARIANTS_SMALL(FA_VARIANT16, 64, 1),
     FA_VARIANTS_SMALL(FA_VARIANT16, 128, 0), FA_VARIANTS_SMALL(FA_VARIANT16, 128, 1),
     FA_VARIANT16(256, 0, 1, 4, 32), FA_VARIANT16(256, 1, 1, 4, 32),
+    // 12 wavefronts (three per SIMD) at d = 64, non-causal: grids that 384-query
+    // tiles spread more evenly over the compute units than 256-query tiles
+    FA_VARIANT(64, 0, 1, 12, 64), FA_VARIANT16(64, 0, 1, 12, 64),
     // one wavefront of 32 queries: the split path's tile for decoding (Nq <= 32)
     FA_VARIANT(64, 0, 1, 1, 64), FA_VARIANT(64, 1, 1, 1, 64), FA_VARIANT(128, 0, 1, 1, 32),
     FA_VARIANT(128, 1, 1, 1, 32), FA_VARIANT16(64, 0, 1, 1, 64), FA_VARIANT16(64, 1, 1, 1, 64),
@@ -175,20 +178,40 @@ int check_device(int* cus = nullptr) {
 }
 
 // The tile a launch uses when the caller names none: default_cfg_dt, except
-// on grids smaller than the GPU.  An 8-wavefront grid (B*H*ceil(Nq/256)
-// workgroups, one per CU at a time) with fewer workgroups than compute units
-// takes 4-wavefront tiles, which doubles its workgroups; at d = 64 and 128 a
-// 4-wavefront grid that still leaves compute units idle takes one-wavefront
-// tiles (32 queries per workgroup, four times the workgroups again; 32-key
-// tiles at d = 128).
+// on grids that would leave compute units idle or unevenly loaded.
+// * An 8-wavefront grid (B*H*ceil(Nq/256) workgroups, one per CU at a time)
+//   with fewer workgroups than compute units takes 4-wavefront tiles, which
+//   doubles its workgroups; at d = 64 and 128 a 4-wavefront grid that still
+//   leaves compute units idle takes one-wavefront tiles (32 queries per
+//   workgroup, four times the workgroups again; 32-key tiles at d = 128).
+// * Non-causal grids at d = 64 and 128 that fill the GPU: every query tile
+//   costs the same, so a launch lasts about as long as the busiest CU, which
+//   runs ceil(workgroups / CUs) tiles of `waves` wavefronts each.  Of the
+//   8-, 12- (d = 64) and 4-wavefront tiles the one with the least such work
+//   is taken, each weighed by its measured speed on grids that divide evenly
+//   (per mille of the 8-wavefront tile's time: 12 waves 975, 4 waves 1030 at
+//   d = 64 and 1050 at d = 128); ties keep the 8-wavefront tile.
 fa_tile_cfg launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, int cus) {
   fa_tile_cfg c = default_cfg_dt(Nq, d, causal, dtype);
   auto wgs = [&](const fa_tile_cfg& t) {
     return (long long)B * H * ((Nq + t.qb * t.waves * 32 - 1) / (t.qb * t.waves * 32));
   };
-  if (c.waves == 8 && wgs(c) < cus) c = fa_tile_cfg{1, 4, 64};
-  const fa_tile_cfg one{1, 1, d == 128 ? 32 : 64};
-  if ((d == 64 || d == 128) && c.waves == 4 && wgs(c) < cus && find_variant(d, causal, one, dtype)) c = one;
+  if (c.waves == 8 && wgs(c) < cus) {
+    c = fa_tile_cfg{1, 4, 64};
+    const fa_tile_cfg one{1, 1, d == 128 ? 32 : 64};
+    if ((d == 64 || d == 128) && wgs(c) < cus && find_variant(d, causal, one, dtype)) c = one;
+    return c;
+  }
+  if (c.waves == 8 && !causal && (d == 64 || d == 128) && cus > 0) {
+    struct Option { fa_tile_cfg t; long long permille; };
+    const Option opts[] = {{{1, 8, 64}, 1000}, {{1, 12, 64}, 975}, {{1, 4, 64}, d == 64 ? 1030 : 1050}};
+    long long best = -1;
+    for (const Option& o : opts) {
+      if (!find_variant(d, causal, o.t, dtype)) continue;
+      const long long cost = (wgs(o.t) + cus - 1) / cus * o.t.waves * o.permille;
+      if (best < 0 || cost < best) best = cost, c = o.t;
+    }
+  }
   return c;
 }
 

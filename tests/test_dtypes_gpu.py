@@ -58,6 +58,24 @@ def test_dtype_and_head_dim(dtype, d, causal, Nq, Nk):
     check(q, k, v, causal, dtype, "%s d=%d c=%d Nq=%d Nk=%d" % (dtype, d, causal, Nq, Nk), run)
 
 
+def f16_variants():
+    import flashattention_forward_fa2_amd as fa
+    try:
+        return fa.variants("f16")
+    except Exception:
+        return []
+
+
+@pytest.mark.parametrize("variant", f16_variants(), ids=lambda v: "d%d-c%d-qb%d-w%d-bk%d" % (v[0], v[1], *v[2]))
+def test_every_compiled_f16_variant(variant):
+    """Each fp16 tile configuration, named explicitly, on a head of several ragged tiles."""
+    import flashattention_forward_fa2_amd as fa
+    d, causal, cfg = variant
+    q, k, v = qkv(8300 + d + causal, 2, 3, 600, 600, d, "f16", sigma=2.0)
+    run = lambda a, b, c: fa.fa_fwd_ex(a, b, c, scale=fp32_scale(d), causal=bool(causal), cfg=cfg)
+    check(q, k, v, causal, "f16", "f16 variant d=%d c=%d %s" % (d, causal, cfg), run)
+
+
 @pytest.mark.parametrize("d", [32, 256])
 @pytest.mark.parametrize("causal", [0, 1])
 def test_fa_fwd_bf16_new_head_dims(d, causal):

@@ -1,7 +1,9 @@
 """The tile fa_fwd picks on its own (fa_launch_cfg): 8-wavefront tiles when the
 grid fills the GPU, 4-wavefront tiles when it would not, one-wavefront tiles at
-d = 64 and 128 when even those would not, and the default launch is bit-identical to the
-explicit launch of the configuration it names."""
+d = 64 and 128 when even those would not; on non-causal grids that fill the GPU,
+the 8-, 12- or 4-wavefront tile that leaves the busiest compute unit the least
+work; and the default launch is bit-identical to the explicit launch of the
+configuration it names."""
 import numpy as np
 import pytest
 
@@ -39,11 +41,40 @@ def test_choice_follows_the_grid():
     assert fa.launch_cfg(1, 8, n - 256, 64, False) == (1, 4, 64)      # 8 * (ceil(cus / 8) - 1) < cus
 
 
-@pytest.mark.parametrize("N,causal", [(1024, True), (1024, False), (4096, False), (300, True)])
+def balanced(B, H, N, waves, permille, cus):
+    n = B * H * -(-N // (32 * waves))
+    return -(-n // cus) * waves * permille
+
+
+@pytest.mark.parametrize("B,H,N,d", [(4, 8, 4096, 64), (4, 8, 3072, 64), (4, 8, 6144, 64), (4, 12, 2048, 64),
+                                     (2, 16, 5000, 64), (1, 64, 3000, 64), (4, 32, 8192, 128),
+                                     (4, 8, 3072, 128), (2, 16, 5000, 128), (4, 16, 4096, 128)])
+def test_non_causal_tile_balances_the_compute_units(B, H, N, d):
+    import torch
+    import flashattention_forward_fa2_amd as fa
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if B * H * -(-N // 256) < cus:
+        pytest.skip("grid smaller than the device: the small-grid rule applies")
+    opts = [((1, 8, 64), 1000), ((1, 12, 64), 975), ((1, 4, 64), 1030 if d == 64 else 1050)]
+    if d != 64:
+        opts.pop(1)
+    want = min(opts, key=lambda o: (balanced(B, H, N, o[0][1], o[1], cus), o[0] != (1, 8, 64)))[0]
+    for dt in ("bf16", "f16"):
+        assert fa.launch_cfg(B, H, N, d, False, dt) == want
+    assert fa.launch_cfg(B, H, N, d, True) in ((1, 8, 64),)                 # causal keeps the 8-wave tile
+    if cus == 256:                                                         # the measured choices on MI355X
+        assert dict([((4, 8, 4096, 64), (1, 8, 64)), ((4, 8, 3072, 64), (1, 12, 64)),
+                     ((4, 8, 6144, 64), (1, 12, 64)), ((4, 12, 2048, 64), (1, 4, 64)),
+                     ((2, 16, 5000, 64), (1, 4, 64)), ((1, 64, 3000, 64), (1, 12, 64)),
+                     ((4, 32, 8192, 128), (1, 8, 64)), ((4, 8, 3072, 128), (1, 4, 64)),
+                     ((2, 16, 5000, 128), (1, 4, 64)), ((4, 16, 4096, 128), (1, 8, 64))])[(B, H, N, d)] == want
+
+
+@pytest.mark.parametrize("N,causal", [(1024, True), (1024, False), (4096, False), (300, True), (3072, False)])
 def test_default_launch_equals_the_named_configuration(N, causal):
     import torch
     import flashattention_forward_fa2_amd as fa
-    B, H = 1, 8
+    B, H = (4, 8) if N == 3072 else (1, 8)
     d = 128 if N == 300 else 64
     q, k, v = (to_device(a) for a in random_qkv(7700 + N, B, H, N, d))
     scale = fp32_scale(d)
