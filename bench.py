@@ -298,7 +298,7 @@ def main():
         del q, k, v, outs, lses
         torch.cuda.empty_cache()
         ramp = min(0.3, args.ramp_seconds)
-        fl = 5 if args.flush_reps > 0 else 0
+        fl = max(0, args.flush_reps)
         rec["targets"] = {"B1-H32-N32768-d128 causal": other_workload(4, [1], args.extra_steps, fl, 8, ramp),
                           "B4-H32-N8192-d128-peaked non-causal": other_workload(5, [0], args.extra_steps, fl, 8, ramp)}
         rec["short_configs"] = {"B1-H1-N256-d64": other_workload(1, [0], 50, 4 * fl, None, ramp),
