@@ -86,6 +86,9 @@ def parse():
     ap.add_argument("--extra-steps", type=int, default=10, help="timed launches per mode of workloads 4 and 5")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="instead of attention, run a plain device copy of MIB MiB (calibrates byte counters)")
+    ap.add_argument("--gemm-only", type=int, default=0, metavar="REPS",
+                    help="instead of attention, time REPS 8192^3 bf16 GEMMs (torch.mm) after a 1 s ramp "
+                         "(the roofline's attainable-GEMM reference alone)")
     return ap.parse_args()
 
 
@@ -113,6 +116,11 @@ def main():
 
     if args.copy_calib:
         copy_calibration(args.copy_calib)
+        return
+    if args.gemm_only:
+        import torch
+        tflops = attainable_gemm(torch, torch.device("cuda:0"), reps=args.gemm_only)
+        print(json.dumps({"gemm": "8192^3 bf16 torch.mm", "tflops": tflops}), flush=True)
         return
     if args.bwd:
         main_bwd(args)
@@ -521,14 +529,20 @@ def main_bwd(args):
     print(json.dumps(rec), flush=True)
 
 
-def attainable_gemm(torch, dev, n=8192, reps=10):
+def attainable_gemm(torch, dev, n=8192, reps=20, ramp_seconds=1.0):
     """A large dense bf16 GEMM through torch (hipBLASLt) on the same GPU: the MFMA
-    rate a library reaches here, reported beside the nominal peak."""
+    rate a library reaches here, reported beside the nominal peak.  Timed after
+    ramp_seconds of back-to-back GEMMs (its first dispatches run up to a third
+    slower while the clock settles)."""
     a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
     b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
-    for _ in range(3):
-        torch.mm(a, b)
+    torch.mm(a, b)
     torch.cuda.synchronize()
+    t_end = time.time() + ramp_seconds
+    while time.time() < t_end:
+        for _ in range(4):
+            torch.mm(a, b)
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
