@@ -127,3 +127,34 @@ def test_single_query_over_long_keys_equals_last_row():
     out_n, lse_n = run_ex(tq, tk, tv, fp32_scale(d), False)
     o_ref, l_ref = oracle.attention_rows(q1, k, v, fp32_scale(d), False)
     compare(bits_of(out_n), lse_n.cpu().numpy(), o_ref, l_ref, label="decode Nq=1")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_bnhd_on_the_twelve_wavefront_tile(dtype):
+    """[B, N, H, d] views at a non-causal shape whose default tile is the
+    12-wavefront one (B4 H8 N3072 d64 on a 256-CU device: 256 workgroups of 384
+    queries), so the strided instantiation of that tile runs; sampled rows
+    (every 384-query tile's edges and the ragged last one) against the oracle,
+    and bit-identity with the contiguous launch of the same tile."""
+    import torch
+    import flashattention_forward_fa2_amd as fa
+    from inputs import sample_rows
+    B, H, N, d = 4, 8, 3072, 64
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    cfg = fa.launch_cfg(B, H, N, d, False, dtype)
+    if cus == 256:
+        assert cfg == (1, 12, 64)
+    q, k, v = random_qkv(6600, B, H, N, d, dtype=dtype)
+    tq, tk, tv = (to_device(a, dtype=dtype).permute(0, 2, 1, 3).contiguous() for a in (q, k, v))  # [B, N, H, d]
+    out, lse = run_ex(tq.transpose(1, 2), tk.transpose(1, 2), tv.transpose(1, 2), fp32_scale(d), False)
+    rows = sample_rows(6600, B, H, N, per_head=24)
+    extra = np.array([bh * N + i for bh in range(B * H) for i in (383, 384, 767, 768, 2687, 2688)])
+    rows = np.unique(np.concatenate([rows, extra]))
+    o_ref, l_ref = oracle.attention_rows(q, k, v, fp32_scale(d), False, rows=rows, dtype=dtype)
+    tol = dict(o_max=4e-3, o_mean=3e-4) if dtype == "f16" else {}
+    compare(bits_of(out), lse.contiguous().cpu().numpy(), o_ref, l_ref, rows=rows, dtype=dtype,
+            label="bnhd 12-wave tile %s" % dtype, **tol)
+    o2, l2 = fa.fa_fwd_ex(to_device(q, dtype=dtype), to_device(k, dtype=dtype), to_device(v, dtype=dtype),
+                          scale=fp32_scale(d), causal=False, cfg=cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(out.contiguous().view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2)
