@@ -5,7 +5,8 @@ times; the small and mid workloads are compared on every output row, the two
 long ones on a deterministic row sample the oracle computes row by row.  Edge
 cases: ragged N around the tile sizes, every compiled tile variant, the
 closed-form cases (identical keys, causal row 0), a maximum that arrives only in
-the last key tile, determinism and untouched memory around the outputs."""
+the last key tile, a large common offset on every score, extreme softmax scales,
+determinism and untouched memory around the outputs."""
 import math
 
 import numpy as np
@@ -216,3 +217,31 @@ def test_head_near_the_byte_limit(causal):
     o_bits = out.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     o_ref, l_ref = oracle.attention_rows(q, k, v, fp32_scale(d), causal, rows)
     compare(o_bits, lse.cpu().numpy(), o_ref, l_ref, rows=rows, label="2 GB head causal=%d" % causal)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("sign", [1, -1])
+def test_large_common_score_offset(d, causal, sign):
+    """Every score carries the same large offset (one shared component of 64 in
+    q and +-64 in k adds +-4096 to every dot product, +-512 after the 1/8 or
+    1/sqrt(128) scale): softmax is shift invariant, so O must match the oracle
+    and LSE must carry the offset.  Exercises the reference maximum's start
+    and its first move far from zero, in both directions."""
+    N = 700
+    q, k, v = random_qkv(9100 + d + causal, 1, 2, N, d)
+    qf, kf = bf16_bits_to_f64(q), bf16_bits_to_f64(k)
+    qf[..., 0] = 64.0
+    kf[..., 0] = 64.0 * sign
+    q2, k2 = f64_to_bf16_bits(qf).reshape(q.shape), f64_to_bf16_bits(kf).reshape(k.shape)
+    check_rows(q2, k2, v, fp32_scale(d), causal, label="offset %+d d=%d causal=%d" % (sign, d, causal))
+
+
+@pytest.mark.parametrize("scale", [1e-6, 40.0])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_extreme_scales(scale, causal):
+    """A tiny softmax scale (every weight ~1/n: O ~ the mean of the visible V rows)
+    and a large one (weights nearly one-hot), each against the oracle on every row."""
+    N, d = 700, 64
+    q, k, v = random_qkv(9200 + causal, 1, 2, N, d)
+    check_rows(q, k, v, float(np.float32(scale)), causal, label="scale %g causal=%d" % (scale, causal))
