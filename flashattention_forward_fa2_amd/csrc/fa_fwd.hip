@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -27,11 +28,36 @@ struct Variant {
   Launcher launch_split;    // any strides, one key split per workgroup (p.nsplit splits)
 };
 
+int device_cus();
+
+// Workgroups of this kernel resident on one CU at a time (from the occupancy
+// calculator, once per instantiation; at least 1).
+template <int D, bool CAUSAL, int QB, int WAVES, int BK, bool STRIDED, bool SPLIT, typename E>
+int resident_per_cu() {
+  static std::atomic<int> cached{0};
+  int r = cached.load(std::memory_order_relaxed);
+  if (r == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fa::fa_fwd_kernel<D, CAUSAL, QB, WAVES, BK, STRIDED, SPLIT, E>,
+                                                     WAVES * 64, 0) != hipSuccess || n < 1)
+      n = 1;
+    cached.store(n, std::memory_order_relaxed);
+    r = n;
+  }
+  return r;
+}
+
 template <int D, bool CAUSAL, int QB, int WAVES, int BK, bool STRIDED, bool SPLIT, typename E>
 hipError_t launch_variant(const fa::Params& p, int B, hipStream_t stream) {
   using T = fa::Tile<D, QB, WAVES, BK>;
   fa::Params pr = p;
   pr.nqt = (p.Nq + T::kBQ - 1) / T::kBQ;
+  pr.resident = 1;
+  pr.cus = 0;
+  if (CAUSAL && !SPLIT) {
+    pr.resident = resident_per_cu<D, CAUSAL, QB, WAVES, BK, STRIDED, SPLIT, E>();
+    pr.cus = device_cus();
+  }
   const long long blocks = (long long)B * p.H * pr.nqt * (SPLIT ? p.nsplit : 1);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fa::fa_fwd_kernel<D, CAUSAL, QB, WAVES, BK, STRIDED, SPLIT, E>), dim3((unsigned)blocks),
@@ -175,6 +201,12 @@ int check_device(int* cus = nullptr) {
   });
   if (cus) *cus = g_dev_cus[dev];
   return g_dev_ok[dev] ? FA_OK : FA_ERR_NO_DEVICE;
+}
+
+// The current device's compute units (0 when unknown); check_device has run.
+int device_cus() {
+  int cus = 0;
+  return check_device(&cus) == FA_OK ? cus : 0;
 }
 
 // The tile a launch uses when the caller names none: default_cfg_dt, except

@@ -196,6 +196,9 @@ struct Params {
   float* part_o;
   float* part_lse;
   int chunk, nsplit;
+  // Causal launch order (not SPLIT): workgroups resident per CU at a time for
+  // this kernel, and the device's CU count.
+  int resident, cus;
 };
 
 // STRIDED = false: every tensor is contiguous [B, H, N, d] (lse [B, H, Nq]) and
@@ -240,16 +243,32 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
   const int t = xcd ? (i & 7) * (total >> 3) + (i >> 3) : i;
   int bh, qt;
   if (CAUSAL) {
+    // When several workgroups fit on a CU, the first `resident` layers of
+    // `cus` workgroups start together and workgroups b and b + cus share a CU;
+    // every odd full layer then runs in reverse order, so a long tile shares its
+    // CU with a short one instead of one of the same length.
+    const int res = SPLIT ? 1 : pr.resident;
     if (xcd) {
       const int per = total >> 3, hpx = BH >> 3;
-      const int chunk = t / per, j = t - chunk * per;
+      const int chunk = t / per;
+      int j = t - chunk * per;
+      const int cpx = pr.cus >> 3;  // CUs per XCD
+      if (res > 1 && cpx > 0 && (pr.cus & 7) == 0) {
+        const int l = j / cpx, p = j - l * cpx;
+        if ((l & 1) && l < res && (l + 1) * cpx <= per) j = l * cpx + (cpx - 1 - p);
+      }
       const int gs = (hpx % FA_CAUSAL_GROUP) == 0 ? FA_CAUSAL_GROUP : hpx;
       const int grp = j / (gs * nqt), r = j - grp * gs * nqt;
       bh = chunk * hpx + grp * gs + r % gs;
       qt = nqt - 1 - r / gs;
     } else {
-      bh = t % BH;
-      qt = nqt - 1 - t / BH;
+      int u = t;
+      if (res > 1 && pr.cus > 0) {
+        const int l = u / pr.cus, p = u - l * pr.cus;
+        if ((l & 1) && l < res && (l + 1) * pr.cus <= total) u = l * pr.cus + (pr.cus - 1 - p);
+      }
+      bh = u % BH;
+      qt = nqt - 1 - u / BH;
     }
   } else {
     bh = t / nqt;

@@ -245,3 +245,14 @@ def test_extreme_scales(scale, causal):
     N, d = 700, 64
     q, k, v = random_qkv(9200 + causal, 1, 2, N, d)
     check_rows(q, k, v, float(np.float32(scale)), causal, label="scale %g causal=%d" % (scale, causal))
+
+
+@pytest.mark.parametrize("B,H,N,d,cfg", [(4, 8, 4096, 32, None), (4, 8, 4096, 64, (1, 4, 64)), (3, 11, 4096, 32, None)])
+def test_causal_order_with_several_workgroups_per_cu(B, H, N, d, cfg):
+    """Causal launches whose kernel keeps several workgroups on a CU (d = 32: two;
+    the 4-wavefront d = 64 tile: three) run every other layer of co-resident
+    workgroups in reverse order, on the XCD-grouped order (B*H a multiple of 8)
+    and on the plain one (B*H = 33); every row against the oracle, so a query
+    tile skipped or computed twice by the reordering would show."""
+    q, k, v = random_qkv(9300 + d + H, B, H, N, d)
+    check_rows(q, k, v, fp32_scale(d), 1, cfg=cfg, label="causal order B%d H%d d%d cfg %s" % (B, H, d, cfg))
