@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -40,15 +41,33 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 constexpr int kMaxDevices = 64;
 std::once_flag g_dev_once[kMaxDevices];
 int g_dev_ok[kMaxDevices];
+int g_dev_cus[kMaxDevices];
 
-int check_device() {
+// FA_OK with *cus = the current device's compute units, or FA_ERR_NO_DEVICE.
+int check_device(int* cus = nullptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_NO_DEVICE;
   std::call_once(g_dev_once[dev], [dev] {
     hipDeviceProp_t p;
     g_dev_ok[dev] = hipGetDeviceProperties(&p, dev) == hipSuccess && std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    g_dev_cus[dev] = g_dev_ok[dev] ? p.multiProcessorCount : 0;
   });
+  if (cus) *cus = g_dev_cus[dev];
   return g_dev_ok[dev] ? FA_OK : FA_ERR_NO_DEVICE;
+}
+
+// Workgroups of `kernel` (launched with `threads` per workgroup) resident on one
+// CU at a time, from the occupancy calculator, cached by the caller; at least 1.
+template <typename K>
+int occupancy(std::atomic<int>& cached, K kernel, int threads) {
+  int r = cached.load(std::memory_order_relaxed);
+  if (r == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) n = 1;
+    cached.store(n, std::memory_order_relaxed);
+    r = n;
+  }
+  return r;
 }
 
 int check_sizes(int B, int H, int N, int d) {
@@ -183,12 +202,22 @@ hipError_t launch(const fa::BwdParams& p0, hipStream_t stream) {
   hipLaunchKernelGGL((fa::fa_bwd_pre_kernel<D, E, STRIDED>), dim3((unsigned)pre_blocks), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  static std::atomic<int> dkdv_res{0}, dq_res{0};
+  p.resident = 1;
+  p.cus = 0;
+  if (CAUSAL) {
+    check_device(&p.cus);
+    p.resident = occupancy(dkdv_res, fa::fa_bwd_dkdv_kernel<D, CAUSAL, kDkdvWaves<D>, kDkdvVlds<D>, E, STRIDED>,
+                           kDkdvWaves<D> * 64);
+  }
   constexpr int kBK = kDkdvWaves<D> * 32;
   p.ntiles = (p.Nk + kBK - 1) / kBK;  // key tiles
   hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<D, CAUSAL, kDkdvWaves<D>, kDkdvVlds<D>, E, STRIDED>),
                      dim3((unsigned)(p.BH * p.ntiles)), dim3(kDkdvWaves<D> * 64), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (CAUSAL) p.resident = occupancy(dq_res, fa::fa_bwd_dq_kernel<D, CAUSAL, kDqWaves, kDqBK<D>, E, STRIDED>,
+                                     kDqWaves * 64);
   constexpr int kBQ = kDqWaves * 32;
   p.ntiles = (p.Nq + kBQ - 1) / kBQ;  // query tiles
   hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<D, CAUSAL, kDqWaves, kDqBK<D>, E, STRIDED>),

@@ -69,6 +69,9 @@ struct BwdParams {
   int nqt;  // query tiles of 64 rows per head: ceil(Nq / 64)
   float qk_scale;  // scale * log2(e)
   float scale;
+  // Causal launch order: workgroups of the launched kernel resident per CU at a
+  // time, and the device's CU count (set per launch).
+  int resident, cus;
 };
 
 // Element offset of head bh of a tensor: strided, or contiguous [B, H, rows, D].
@@ -166,18 +169,33 @@ __device__ __forceinline__ void pack_b(const f32x16& x, typename E::v8 (&b)[2]) 
 // when the head count allows, so that each XCD works through a contiguous set
 // of heads; `rank` 0 is the tile to run first (the caller maps it to its
 // longest tile when causal).
-__device__ __forceinline__ void tile_of(int i, int total, int BH, int ntiles, bool causal, int& bh, int& rank) {
+__device__ __forceinline__ void tile_of(int i, int total, int BH, int ntiles, bool causal, int resident, int cus,
+                                        int& bh, int& rank) {
   const bool xcd = (BH % 8) == 0;
   const int t = xcd ? (i & 7) * (total >> 3) + (i >> 3) : i;
   if (causal) {
+    // With several workgroups resident per CU, the first `resident` layers of
+    // `cus` workgroups start together and workgroups i and i + cus share a CU:
+    // every odd full layer runs in reverse, pairing long tiles with short ones.
     if (xcd) {
       const int per = total >> 3, hpx = BH >> 3;
-      const int chunk = t / per, j = t - chunk * per;
+      const int chunk = t / per;
+      int j = t - chunk * per;
+      const int cpx = cus >> 3;
+      if (resident > 1 && cpx > 0 && (cus & 7) == 0) {
+        const int l = j / cpx, p = j - l * cpx;
+        if ((l & 1) && l < resident && (l + 1) * cpx <= per) j = l * cpx + (cpx - 1 - p);
+      }
       bh = chunk * hpx + j % hpx;
       rank = j / hpx;
     } else {
-      bh = t % BH;
-      rank = t / BH;
+      int u = t;
+      if (resident > 1 && cus > 0) {
+        const int l = u / cus, p = u - l * cus;
+        if ((l & 1) && l < resident && (l + 1) * cus <= total) u = l * cus + (cus - 1 - p);
+      }
+      bh = u % BH;
+      rank = u / BH;
     }
   } else {
     bh = t / ntiles;
@@ -245,7 +263,7 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
   const int g = lane >> 5, lr = lane & 31;
 
   int bh, kt;
-  tile_of((int)blockIdx.x, (int)gridDim.x, pr.BH, pr.ntiles, CAUSAL, bh, kt);
+  tile_of((int)blockIdx.x, (int)gridDim.x, pr.BH, pr.ntiles, CAUSAL, pr.resident, pr.cus, bh, kt);
   const int q_rs = STRIDED ? pr.q_rs : D, do_rs = STRIDED ? pr.do_rs : D;
   const int k_rs = STRIDED ? pr.k_rs : D, v_rs = STRIDED ? pr.v_rs : D;
   const __amdgpu_buffer_rsrc_t qrs =
@@ -453,7 +471,7 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams p
   const int g = lane >> 5, lr = lane & 31;
 
   int bh, rank;
-  tile_of((int)blockIdx.x, (int)gridDim.x, pr.BH, nqt, CAUSAL, bh, rank);
+  tile_of((int)blockIdx.x, (int)gridDim.x, pr.BH, nqt, CAUSAL, pr.resident, pr.cus, bh, rank);
   const int qt = CAUSAL ? nqt - 1 - rank : rank;  // causal: longest (last) query tile first
   const int q_rs = STRIDED ? pr.q_rs : D, do_rs = STRIDED ? pr.do_rs : D;
   const int k_rs = STRIDED ? pr.k_rs : D, v_rs = STRIDED ? pr.v_rs : D;
