@@ -216,13 +216,13 @@ int device_cus() {
 //   doubles its workgroups; at d = 64 and 128 a 4-wavefront grid that still
 //   leaves compute units idle takes one-wavefront tiles (32 queries per
 //   workgroup, four times the workgroups again; 32-key tiles at d = 128).
-// * Non-causal grids at d = 64 and 128 that fill the GPU: every query tile
+// * Non-causal grids at d = 32, 64 and 128 that fill the GPU: every query tile
 //   costs the same, so a launch lasts about as long as the busiest CU, which
 //   runs ceil(workgroups / CUs) tiles of `waves` wavefronts each.  Of the
 //   8-, 12- (d = 64) and 4-wavefront tiles the one with the least such work
 //   is taken, each weighed by its measured speed on grids that divide evenly
-//   (per mille of the 8-wavefront tile's time: 12 waves 975, 4 waves 1030 at
-//   d = 64 and 1050 at d = 128); ties keep the 8-wavefront tile.
+//   (per mille of the 8-wavefront tile's time: 12 waves 975, 4 waves 1025 at
+//   d = 32, 1030 at d = 64 and 1050 at d = 128); ties keep the 8-wavefront tile.
 fa_tile_cfg launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, int cus) {
   fa_tile_cfg c = default_cfg_dt(Nq, d, causal, dtype);
   auto wgs = [&](const fa_tile_cfg& t) {
@@ -234,9 +234,9 @@ fa_tile_cfg launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, int c
     if ((d == 64 || d == 128) && wgs(c) < cus && find_variant(d, causal, one, dtype)) c = one;
     return c;
   }
-  if (c.waves == 8 && !causal && (d == 64 || d == 128) && cus > 0) {
+  if (c.waves == 8 && !causal && (d == 32 || d == 64 || d == 128) && cus > 0) {
     struct Option { fa_tile_cfg t; long long permille; };
-    const Option opts[] = {{{1, 8, 64}, 1000}, {{1, 12, 64}, 975}, {{1, 4, 64}, d == 64 ? 1030 : 1050}};
+    const Option opts[] = {{{1, 8, 64}, 1000}, {{1, 12, 64}, 975}, {{1, 4, 64}, d == 32 ? 1025 : d == 64 ? 1030 : 1050}};
     long long best = -1;
     for (const Option& o : opts) {
       if (!find_variant(d, causal, o.t, dtype)) continue;

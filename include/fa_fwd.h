@@ -213,12 +213,12 @@ int fa_default_cfg(int N, int d, int causal, fa_tile_cfg *cfg);
  * count, the 4-wavefront tile (1, 4, 64), which doubles the workgroups, and at
  * d = 64 or 128 (bf16 or fp16), when that grid too is smaller, the
  * one-wavefront tile (1, 1, 64), or (1, 1, 32) at d = 128.  Non-causal
- * launches at d = 64 or 128 (bf16 or fp16) whose 8-wavefront grid fills the
- * device take, of (1, 8, 64), (1, 12, 64) (d = 64 only) and (1, 4, 64), the
- * tile that leaves the busiest compute unit the least work:
+ * launches at d = 32, 64 or 128 (bf16 or fp16) whose 8-wavefront grid fills
+ * the device take, of (1, 8, 64), (1, 12, 64) (d = 64 only) and (1, 4, 64),
+ * the tile that leaves the busiest compute unit the least work:
  * ceil(workgroups / CUs) * waves, weighed by the tile's speed on evenly
- * divided grids (8 waves 1.000, 12 waves 0.975, 4 waves 1.030 at d = 64 and
- * 1.050 at d = 128); ties keep (1, 8, 64).
+ * divided grids (8 waves 1.000, 12 waves 0.975, 4 waves 1.025 at d = 32,
+ * 1.030 at d = 64 and 1.050 at d = 128); ties keep (1, 8, 64).
  * FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_ARG (causal, dtype)
  * or FA_ERR_NO_DEVICE. */
 int fa_launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, fa_tile_cfg *cfg);
