@@ -37,10 +37,12 @@ class FaError(RuntimeError):
 
 
 class TileCfg(ctypes.Structure):
-    _fields_ = [("qb", ctypes.c_int), ("waves", ctypes.c_int), ("bk", ctypes.c_int)]
+    """fa_tile_cfg: (qb, waves, bk) or, for the key-split tile, (qb, waves, bk, ksplit)."""
+    _fields_ = [("qb", ctypes.c_int), ("waves", ctypes.c_int), ("bk", ctypes.c_int), ("ksplit", ctypes.c_int)]
 
     def as_tuple(self):
-        return (self.qb, self.waves, self.bk)
+        t = (self.qb, self.waves, self.bk)
+        return t + (self.ksplit,) if self.ksplit > 1 else t
 
 
 _LL3 = ctypes.c_longlong * 3
@@ -164,7 +166,8 @@ def default_cfg(N: int, d: int, causal: bool):
 
 
 def launch_cfg(B: int, H: int, Nq: int, d: int, causal: bool, dtype: str = "bf16"):
-    """The ``(qb, waves, bk)`` tile fa_fwd / fa_fwd_ex launch for these sizes on the current device."""
+    """The tile fa_fwd / fa_fwd_ex launch for these sizes on the current device: ``(qb, waves, bk)``, or
+    ``(qb, waves, bk, ksplit)`` for the key-split tile."""
     c = TileCfg()
     _check(load_library().fa_launch_cfg(int(B), int(H), int(Nq), int(d), int(bool(causal)), _DTYPE_NAMES[dtype],
                                         ctypes.byref(c)))
@@ -173,7 +176,7 @@ def launch_cfg(B: int, H: int, Nq: int, d: int, causal: bool, dtype: str = "bf16
 
 def variants(dtype: str = "bf16"):
     """Compiled variants of one element type ("bf16", "f16" or "f32") as
-    (d, causal, (qb, waves, bk)) tuples."""
+    (d, causal, cfg) tuples, cfg as ``TileCfg.as_tuple`` gives it."""
     lib = load_library()
     want = _DTYPE_NAMES[dtype]
     out = []

@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int kVersion = 501;  // 0.5.1
+constexpr int kVersion = 600;  // 0.6.0: fa_tile_cfg.ksplit
 
 using Launcher = hipError_t (*)(const fa::Params&, int B, hipStream_t);
 
@@ -26,7 +26,11 @@ struct Variant {
   Launcher launch;          // contiguous [B, H, N, d] tensors
   Launcher launch_strided;  // any strides
   Launcher launch_split;    // any strides, one key split per workgroup (p.nsplit splits)
+  int ksplit;               // wavefronts splitting one query block's keys (0 or 1: none)
 };
+
+// 0 and 1 both mean "each wavefront owns its own queries".
+int ksplit_of(int k) { return k > 1 ? k : 1; }
 
 int device_cus();
 
@@ -62,6 +66,18 @@ hipError_t launch_variant(const fa::Params& p, int B, hipStream_t stream) {
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fa::fa_fwd_kernel<D, CAUSAL, QB, WAVES, BK, STRIDED, SPLIT, E>), dim3((unsigned)blocks),
                      dim3(T::kThreads), 0, stream, pr);
+  return hipGetLastError();
+}
+
+// Key split inside the workgroup: S wavefronts share each block of 32 queries.
+template <int D, bool CAUSAL, int S, int BK, bool STRIDED, typename E>
+hipError_t launch_wsplit(const fa::Params& p, int B, hipStream_t stream) {
+  fa::Params pr = p;
+  pr.nqt = (p.Nq + 31) / 32;
+  const long long blocks = (long long)B * p.H * pr.nqt;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fa::fa_fwd_wsplit_kernel<D, CAUSAL, S, BK, STRIDED, E>), dim3((unsigned)blocks), dim3(S * 64), 0,
+                     stream, pr);
   return hipGetLastError();
 }
 
@@ -111,6 +127,13 @@ hipError_t run_merge(const fa::Params& p, int d, int dtype, hipStream_t s) {
 #define FA_VARIANT32(D, C, W, BK)                                                                        \
   {D, C, 1, W, BK, FA_DTYPE_F32, &launch_f32<D, (C) != 0, W, BK, false>, &launch_f32<D, (C) != 0, W, BK, true>, \
    nullptr}
+// The key-split tile (1, 4, 32) with ksplit 4: four wavefronts per 32-query
+// block, 32-key tiles in a ring per wavefront (64 KB of LDS at d = 64, 128 KB at
+// d = 128); no split-path launcher.
+#define FA_VARIANT_KS(D, C, T, DT)                                                                     \
+  {D, C, 1, 4, 32, DT, &launch_wsplit<D, (C) != 0, 4, 32, false, T>, &launch_wsplit<D, (C) != 0, 4, 32, true, T>, \
+   nullptr, 4}
+#define FA_VARIANTS_KS(D, C) FA_VARIANT_KS(D, C, fa::Bf16, FA_DTYPE_BF16), FA_VARIANT_KS(D, C, fa::F16, FA_DTYPE_F16)
 #define FA_VARIANTS_DC(D, C) \
   FA_VARIANT(D, C, 1, 4, 64), FA_VARIANT(D, C, 2, 4, 64), FA_VARIANT(D, C, 1, 8, 64)
 // Head dims 32 and 256 and the fp16 element type: the default tile and the
@@ -134,12 +157,14 @@ const Variant kVariants[] = {
     FA_VARIANT16(128, 0, 1, 1, 32), FA_VARIANT16(128, 1, 1, 1, 32),
     FA_VARIANT32(64, 0, 4, 32), FA_VARIANT32(64, 1, 4, 32), FA_VARIANT32(128, 0, 4, 32),
     FA_VARIANT32(128, 1, 4, 32),
+    FA_VARIANTS_KS(64, 0), FA_VARIANTS_KS(64, 1), FA_VARIANTS_KS(128, 0), FA_VARIANTS_KS(128, 1),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 const Variant* find_variant(int d, int causal, const fa_tile_cfg& c, int dtype = FA_DTYPE_BF16) {
   for (const Variant& v : kVariants)
-    if (v.d == d && v.causal == causal && v.dtype == dtype && v.qb == c.qb && v.waves == c.waves && v.bk == c.bk)
+    if (v.d == d && v.causal == causal && v.dtype == dtype && v.qb == c.qb && v.waves == c.waves && v.bk == c.bk &&
+        ksplit_of(v.ksplit) == ksplit_of(c.ksplit))
       return &v;
   return nullptr;
 }
@@ -212,10 +237,13 @@ int device_cus() {
 // The tile a launch uses when the caller names none: default_cfg_dt, except
 // on grids that would leave compute units idle or unevenly loaded.
 // * An 8-wavefront grid (B*H*ceil(Nq/256) workgroups, one per CU at a time)
-//   with fewer workgroups than compute units takes 4-wavefront tiles, which
-//   doubles its workgroups; at d = 64 and 128 a 4-wavefront grid that still
-//   leaves compute units idle takes one-wavefront tiles (32 queries per
-//   workgroup, four times the workgroups again; 32-key tiles at d = 128).
+//   with fewer workgroups than compute units: at d = 64 and 128 (bf16, fp16)
+//   the key-split tile (1, 4, 32, ksplit 4: four wavefronts share each block of
+//   32 queries and split its keys) when causal, or when the 4-wavefront grid
+//   too leaves compute units idle; otherwise 4-wavefront tiles, which double
+//   the workgroups (and, where no key-split tile is compiled, one-wavefront
+//   tiles when those still leave compute units idle).  Causal work is uneven
+//   across query blocks, and the key split evens it inside each workgroup.
 // * Non-causal grids at d = 32, 64 and 128 that fill the GPU: every query tile
 //   costs the same, so a launch lasts about as long as the busiest CU, which
 //   runs ceil(workgroups / CUs) tiles of `waves` wavefronts each.  Of the
@@ -229,6 +257,8 @@ fa_tile_cfg launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, int c
     return (long long)B * H * ((Nq + t.qb * t.waves * 32 - 1) / (t.qb * t.waves * 32));
   };
   if (c.waves == 8 && wgs(c) < cus) {
+    const fa_tile_cfg ks{1, 4, 32, 4};
+    if ((causal || wgs(fa_tile_cfg{1, 4, 64}) < cus) && find_variant(d, causal, ks, dtype)) return ks;
     c = fa_tile_cfg{1, 4, 64};
     const fa_tile_cfg one{1, 1, d == 128 ? 32 : 64};
     if ((d == 64 || d == 128) && wgs(c) < cus && find_variant(d, causal, one, dtype)) c = one;
@@ -572,6 +602,7 @@ int fa_launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, fa_tile_cf
     const int st = check_device(&cus);
     if (st != FA_OK) return st;
     *cfg = launch_cfg(B, H, Nq, d, causal, dtype, cus);
+    cfg->ksplit = ksplit_of(cfg->ksplit);
     return FA_OK;
   } catch (...) {
     return FA_ERR_INTERNAL;
@@ -584,6 +615,7 @@ int fa_default_cfg(int N, int d, int causal, fa_tile_cfg* cfg) {
   if (!head_dim_ok(d)) return FA_ERR_HEAD_DIM;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   *cfg = default_cfg(N, d, causal);
+  cfg->ksplit = 1;
   return FA_OK;
 }
 
@@ -594,7 +626,7 @@ int fa_variant(int i, int* d, int* causal, fa_tile_cfg* cfg) {
   if (!d || !causal || !cfg) return FA_ERR_NULL;
   *d = kVariants[i].d;
   *causal = kVariants[i].causal;
-  *cfg = fa_tile_cfg{kVariants[i].qb, kVariants[i].waves, kVariants[i].bk};
+  *cfg = fa_tile_cfg{kVariants[i].qb, kVariants[i].waves, kVariants[i].bk, ksplit_of(kVariants[i].ksplit)};
   return FA_OK;
 }
 

@@ -552,6 +552,267 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
   }
 }
 
+// s_waitcnt vmcnt(N): at most N of this wavefront's vector memory loads
+// outstanding (N < 64; the count's high bits sit at bits 14..15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Key split inside one workgroup, for grids too small to give every SIMD a
+// wavefront of its own queries.  The workgroup's S wavefronts share ONE block of
+// 32 query rows; wavefront w sweeps key tiles w, w + S, w + 2S, ... through a
+// double-buffered LDS ring of its own, waiting only on its own direct loads (no
+// workgroup barrier in the sweep), and keeps the usual running state (m, l, O)
+// over its keys.  The S partial states of each row are then merged through LDS:
+// with M = max_w m_w and a_w = 2^(m_w - M), O = sum_w a_w O_w / sum_w a_w l_w and
+// LSE = (M + log2 sum_w a_w l_w) ln 2.  This is Flash-Decoding's split of the
+// keys over parallel workers followed by the merge of their partial (m, l, o)
+// states ("FlashAttention and kernels", gtadkapally.com, section
+// "FlashAttention-2, -3, and what came after", the Flash-Decoding paragraph; the
+// merge of two partial states is that page's online max/sum exercise), done
+// inside one launch instead of two.
+template <int D, bool CAUSAL, int S, int BK, bool STRIDED, typename E = Bf16>
+__global__ __launch_bounds__(S * 64) void fa_fwd_wsplit_kernel(const Params pr) {
+  constexpr int kTileBytes = BK * D * 2;
+  constexpr int kBlocks = kTileBytes / 1024;
+  constexpr int kStage = 2 * kTileBytes;  // K then V
+  constexpr int KS = D / 16, DB = D / 32;
+  static_assert(S * 32 * D * 4 <= S * kStage, "merge buffer fits the first ring stage");
+  static_assert(kTileBytes % 1024 == 0 && BK % 32 == 0, "tile");
+  using v8 = typename E::v8;
+  const int Nq = pr.Nq, Nk = pr.Nk, BH = pr.BH;
+  const float qk_scale = pr.qk_scale;
+  const int q_rs = STRIDED ? pr.q_rs : D, k_rs = STRIDED ? pr.k_rs : D;
+  const int v_rs = STRIDED ? pr.v_rs : D, o_rs = STRIDED ? pr.o_rs : D;
+  __shared__ __attribute__((aligned(1024))) char lds0[S * kStage];
+  __shared__ __attribute__((aligned(1024))) char lds1[S * kStage];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, lr = lane & 31;
+  // Causal: the longest query blocks first (one per head, then the next).
+  const int nqt = pr.nqt;
+  int bh, qt;
+  if (CAUSAL) {
+    bh = (int)(blockIdx.x % BH);
+    qt = nqt - 1 - (int)(blockIdx.x / BH);
+  } else {
+    bh = (int)(blockIdx.x / nqt);
+    qt = (int)(blockIdx.x % nqt);
+  }
+  const int batch = bh / pr.H, hd = bh - batch * pr.H;
+  const long long q_off = STRIDED ? batch * pr.q_sb + hd * pr.q_sh : (long long)bh * Nq * D;
+  const long long k_off = STRIDED ? batch * pr.k_sb + hd * pr.k_sh : (long long)bh * Nk * D;
+  const long long v_off = STRIDED ? batch * pr.v_sb + hd * pr.v_sh : (long long)bh * Nk * D;
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(pr.q + q_off, (uint32_t)((Nq - 1) * q_rs + D) * 2);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(pr.k + k_off, (uint32_t)((Nk - 1) * k_rs + D) * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(pr.v + v_off, (uint32_t)((Nk - 1) * v_rs + D) * 2);
+  const int q0 = qt * 32;
+
+  v8 qreg[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(qrs, ((q0 + lr) * q_rs + ks * 16 + g * 8) * 2, 0, 0);
+    qreg[ks] = __builtin_bit_cast(v8, x);
+  }
+  uint32_t dma_k[kBlocks], dma_v[kBlocks];
+#pragma unroll
+  for (int b = 0; b < kBlocks; ++b) {
+    const int p = b * 64 + lane, row = p / (D / 8), pos = p % (D / 8);
+    const uint32_t col = (pos ^ swz<D>(row)) << 4;
+    dma_k[b] = row * k_rs * 2 + col;
+    dma_v[b] = row * v_rs * 2 + col;
+  }
+  int koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = lds_offset<D>(lr, 2 * ks + g);
+  int voff[DB][2];
+  {
+    const int s = lane >> 4, jj = lane & 15, r = jj >> 2, tt = jj & 3;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int key = 4 * g + r + 8 * hi;
+        const int col = db * 32 + 16 * (s & 1) + 4 * tt;
+        voff[db][hi] = lds_offset<D>(key, col >> 3) + ((col & 4) << 1);
+      }
+  }
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  float m = -__FLT_MAX__, thr = -__FLT_MAX__, l = 0.f;
+
+  // Keys [0, kend) in tiles of BK; this wavefront's are wave, wave + S, ...
+  const int kend = CAUSAL ? min(q0 + 32, Nk) : Nk;
+  const int ntiles = (kend + BK - 1) / BK;  // >= 1
+  const int nmine = ntiles > wave ? (ntiles - 1 - wave) / S + 1 : 0;
+  char* const st0 = lds0 + wave * kStage;
+  char* const st1 = lds1 + wave * kStage;
+
+  auto issue = [&](int j, char* dst) {
+    const uint32_t gk = (uint32_t)(j * BK) * k_rs * 2, gv = (uint32_t)(j * BK) * v_rs * 2;
+#pragma unroll
+    for (int b = 0; b < kBlocks; ++b) {
+      dma16(krs, dst + b * 1024, dma_k[b] + gk);
+      dma16(vrs, dst + kTileBytes + b * 1024, dma_v[b] + gv);
+    }
+  };
+
+  // One key tile: the same steps, layouts and lazy reference maximum as
+  // fa_fwd_kernel's compute_tile, for this wavefront's 32 queries.
+  auto compute_tile = [&](const char* kst, int k0, bool masked) {
+    const char* vst = kst + kTileBytes;
+    f32x16 s[BK / 32];
+#pragma unroll
+    for (int kb = 0; kb < BK / 32; ++kb) {
+      v8 a[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) a[ks] = *reinterpret_cast<const v8*>(kst + kb * 32 * (D * 2) + koff[ks]);
+      s[kb] = E::mfma(a[0], qreg[0], f32x16{});
+#pragma unroll
+      for (int ks = 1; ks < KS; ++ks) s[kb] = E::mfma(a[ks], qreg[ks], s[kb]);
+    }
+    v8 va[DB][BK / 16];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int rowoff = kk * 16 * (D * 2);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vst + rowoff + voff[db][0]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vst + rowoff + voff[db][1]));
+        const u32x4 w = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                         __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+        va[db][kk] = __builtin_bit_cast(v8, w);
+      }
+    if (masked) {
+      const int base = k0 + 4 * g;
+      const int lim = CAUSAL ? min(q0 + lr + 1, Nk) - base : Nk - base;
+#pragma unroll
+      for (int kb = 0; kb < BK / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -__builtin_inff();
+    }
+    float mx = vmax(s[0][0], s[0][1]);
+#pragma unroll
+    for (int kb = 0; kb < BK / 32; ++kb)
+#pragma unroll
+      for (int r = (kb == 0 ? 2 : 0); r < 16; ++r) mx = vmax(mx, s[kb][r]);
+    mx = lane_swap_max(mx);
+    const float mt = mx * qk_scale;
+    const bool moves = mt > thr;
+    if (__builtin_amdgcn_ballot_w64(moves)) {
+      const float m_new = moves ? mt : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      l *= alpha;
+      m = m_new;
+      thr = m_new + kLazyMax;
+    }
+    const float m_sub = m;
+    float rs = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int kb = kk >> 1, h = kk & 1;
+      float e8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        e8[i] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * h + i], qk_scale, -m_sub));
+        rs = (kk == 0 && i == 0) ? e8[i] : rs + e8[i];
+      }
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = E::pack(e8[2 * e], e8[2 * e + 1]);
+      const v8 pk = __builtin_bit_cast(v8, w);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] = E::mfma(va[db][kk], pk, oacc[db]);
+    }
+    l += rs;
+  };
+
+  // Local tile i: the load of tile i + 1 into the other stage (read two steps
+  // ago; those reads completed before their products), then tile i, then the
+  // wait for this wavefront's loads.  Stages are fixed per parity, so the
+  // compiler sees that the loads and the fragment reads touch distinct arrays.
+  auto step = [&](int i, char* cur, char* nxt) {
+    const int j = wave + i * S;
+    if (i + 1 < nmine) issue(j + S, nxt);
+    const int k0 = j * BK;
+    const bool masked = (CAUSAL && (k0 + BK - 1 > q0)) || (k0 + BK > Nk);
+    compute_tile(cur, k0, masked);
+    wait_vmcnt<0>();
+  };
+  if (nmine > 0) {
+    issue(wave, st0);
+    wait_vmcnt<0>();
+  }
+  int i = 0;
+  for (; i + 1 < nmine; i += 2) {
+    step(i, st0, st1);
+    step(i + 1, st1, st0);
+  }
+  if (i < nmine) step(i, st0, st1);
+
+  // ---- merge the S partial states of each query row through LDS ----------------
+  // Every wavefront reaches this barrier once, after its last loads landed; the
+  // rings are then reused: O_w (fp32, 16-byte chunks swizzled by row) in the
+  // first, m_w and l_w in the second.  An empty sweep leaves m_w = -FLT_MAX,
+  // l_w = 0 and O_w = 0, whose weight is 0.
+  __syncthreads();
+  float* po = reinterpret_cast<float*>(lds0);  // [S][32][D]
+  float* pm = reinterpret_cast<float*>(lds1);  // [S][32]
+  float* pl = pm + S * 32;                     // [S][32]
+  const float lt = lane_swap_sum(l);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const f32x4 w = {oacc[db][4 * rr], oacc[db][4 * rr + 1], oacc[db][4 * rr + 2], oacc[db][4 * rr + 3]};
+      const int cw = db * 8 + 2 * rr + g;  // 16-byte chunk, swizzled by row against bank conflicts
+      *reinterpret_cast<f32x4*>(po + (wave * 32 + lr) * D + ((cw ^ (lr & 7)) << 2)) = w;
+    }
+  if (g == 0) {
+    pm[wave * 32 + lr] = m;
+    pl[wave * 32 + lr] = lt;
+  }
+  __syncthreads();
+  // Wavefront w finishes head-dim columns [w D/S, (w + 1) D/S) of the 32 rows.
+  float M = -__FLT_MAX__;
+#pragma unroll
+  for (int p = 0; p < S; ++p) M = fmaxf(M, pm[p * 32 + lr]);
+  float wt[S], L = 0.f;
+#pragma unroll
+  for (int p = 0; p < S; ++p) {
+    wt[p] = __builtin_amdgcn_exp2f(pm[p * 32 + lr] - M);
+    L += wt[p] * pl[p * 32 + lr];
+  }
+  const float inv = 1.0f / L;
+  const int query = q0 + lr;
+  constexpr int CPL = D / S / 2;  // columns per lane
+  static_assert(CPL % 4 == 0, "columns per lane");
+  if (query < Nq) {
+    const long long o_off = STRIDED ? batch * pr.o_sb + hd * pr.o_sh : (long long)bh * Nq * D;
+    uint16_t* orow = pr.out + o_off + (long long)query * o_rs;
+    const int c0 = wave * (D / S) + g * CPL;
+#pragma unroll
+    for (int c = 0; c < CPL; c += 4) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < S; ++p)
+        acc += wt[p] * *reinterpret_cast<const f32x4*>(po + (p * 32 + lr) * D + ((((c0 + c) >> 2) ^ (lr & 7)) << 2));
+      u32x2 w;
+      w[0] = E::pack(acc[0] * inv, acc[1] * inv);
+      w[1] = E::pack(acc[2] * inv, acc[3] * inv);
+      *reinterpret_cast<u32x2*>(orow + c0 + c) = w;
+    }
+    const long long l_off = STRIDED ? batch * pr.l_sb + hd * pr.l_sh : (long long)bh * Nq;
+    if (wave == 0 && g == 0) pr.lse[l_off + query] = (M + log2f(L)) * kLn2;
+  }
+}
+
 // Combine the key splits of every query row: with M = max_s LSE_s and
 // w_s = exp(LSE_s - M), O = sum_s w_s O_s / sum_s w_s and LSE = M + ln sum_s w_s
 // -- the merge rule of two partial (m, l, o) states ("FlashAttention and

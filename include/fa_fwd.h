@@ -78,13 +78,22 @@ int fa_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
            int B, int H, int N, int d, float scale, int causal, void *stream);
 
 /* Tile configuration of one compiled kernel variant:
- *   qb     32-query column blocks owned by each 64-lane wavefront (1 or 2);
- *   waves  wavefronts per workgroup (the workgroup owns waves*qb*32 queries);
- *   bk     keys per K/V tile staged through LDS. */
+ *   qb      32-query column blocks owned by each 64-lane wavefront (1 or 2);
+ *   waves   wavefronts per workgroup;
+ *   bk      keys per K/V tile staged through LDS;
+ *   ksplit  0 or 1: each wavefront owns its queries (the workgroup owns
+ *           waves*qb*32 of them); 4 (with qb 1, waves 4, bk 32): the four
+ *           wavefronts share one block of 32 queries, wavefront w sweeps key
+ *           tiles w, w+4, w+8, ..., and their partial softmax states are merged
+ *           at the end of the workgroup (Flash-Decoding's split of the keys, "FlashAttention
+ *           and kernels", "FlashAttention-2, -3, and what came after").  Values
+ *           returned by the library set 1 for the former.
+ * (Since version 600 the struct has four members; earlier versions had three.) */
 typedef struct fa_tile_cfg {
   int qb;
   int waves;
   int bk;
+  int ksplit;
 } fa_tile_cfg;
 
 /* fa_fwd with an explicit tile configuration (for measurements and sweeps).
@@ -210,9 +219,10 @@ int fa_default_cfg(int N, int d, int causal, fa_tile_cfg *cfg);
 /* The configuration fa_fwd and fa_fwd_ex pick for these sizes and element type
  * on the current device: fa_default_cfg's, except that when its 8-wavefront
  * grid (B*H*ceil(Nq/256) workgroups) is smaller than the device's compute-unit
- * count, the 4-wavefront tile (1, 4, 64), which doubles the workgroups, and at
- * d = 64 or 128 (bf16 or fp16), when that grid too is smaller, the
- * one-wavefront tile (1, 1, 64), or (1, 1, 32) at d = 128.  Non-causal
+ * count: at d = 64 or 128 (bf16 or fp16) the key-split tile (1, 4, 32, ksplit
+ * 4) if causal, or if the 4-wavefront grid (B*H*ceil(Nq/128)) is smaller too;
+ * else the 4-wavefront tile (1, 4, 64), which doubles the workgroups (at d = 32
+ * and 256, and fp32, where no key-split tile is compiled).  Non-causal
  * launches at d = 32, 64 or 128 (bf16 or fp16) whose 8-wavefront grid fills
  * the device take, of (1, 8, 64), (1, 12, 64) (d = 64 only) and (1, 4, 64),
  * the tile that leaves the busiest compute unit the least work:

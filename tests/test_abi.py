@@ -135,6 +135,44 @@ def test_desc_layout_matches_the_header(tmp_path):
                    D.stream.offset, D.dtype.offset]
 
 
+def test_tile_cfg_layout_matches_the_header(tmp_path):
+    """The ctypes mirror of fa_tile_cfg (four ints since version 600) has the C
+    struct's size and offsets."""
+    src = tmp_path / "tc.c"
+    src.write_text(
+        "#include <stdio.h>\n#include <stddef.h>\n#include \"fa_fwd.h\"\n"
+        "int main(void){printf(\"%zu %zu %zu\\n\", sizeof(fa_tile_cfg), offsetof(fa_tile_cfg, bk),"
+        " offsetof(fa_tile_cfg, ksplit)); return 0;}\n")
+    exe = tmp_path / "tc"
+    assert os.system("gcc -I %s -o %s %s" % (os.path.join(ROOT, "include"), exe, src)) == 0
+    got = [int(x) for x in os.popen(str(exe)).read().split()]
+    T = fa.TileCfg
+    assert got == [ctypes.sizeof(T), T.bk.offset, T.ksplit.offset]
+    assert fa.version() >= 600
+
+
+def test_key_split_variants(lib):
+    """The key-split tile (1, 4, 32, ksplit 4) is compiled at d = 64 and 128 for
+    bf16 and fp16, both masks; other key-split shapes, and d = 32, are refused
+    before any device call (FA_ERR_ARG), while a compiled one gets as far as the
+    device check."""
+    for dtype in ("bf16", "f16"):
+        vs = fa.variants(dtype)
+        for d in (64, 128):
+            for causal in (0, 1):
+                assert (d, causal, (1, 4, 32, 4)) in vs
+        assert not any(len(v[2]) == 4 for v in vs if v[0] in (32, 256))
+    assert not any(len(v[2]) == 4 for v in fa.variants("f32"))
+    assert call(d=32, cfg=(1, 4, 32, 4)) == 5
+    assert call(d=64, cfg=(1, 4, 32, 3)) == 5
+    assert call(d=64, cfg=(1, 4, 64, 4)) == 5
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        assert call(d=64, cfg=(1, 4, 32, 4)) == 8
+        assert call(d=128, causal=1, cfg=(1, 4, 32, 4)) == 8
+    assert call(d=64, cfg=(1, 4, 32, 0)) == call(d=64, cfg=(1, 4, 32))  # ksplit 0 is ksplit 1
+
+
 def desc(**kw):
     """A valid square contiguous descriptor on fake pointers, then overrides."""
     B, H, Nq, Nk, d = kw.pop("B", 1), kw.pop("H", 2), kw.pop("Nq", 64), kw.pop("Nk", 64), kw.pop("d", 64)

@@ -66,7 +66,7 @@ def f16_variants():
         return []
 
 
-@pytest.mark.parametrize("variant", f16_variants(), ids=lambda v: "d%d-c%d-qb%d-w%d-bk%d" % (v[0], v[1], *v[2]))
+@pytest.mark.parametrize("variant", f16_variants(), ids=lambda v: "d%d-c%d-%s" % (v[0], v[1], "-".join(map(str, v[2]))))
 def test_every_compiled_f16_variant(variant):
     """Each fp16 tile configuration, named explicitly, on a head of several ragged tiles."""
     import flashattention_forward_fa2_amd as fa

@@ -1,9 +1,10 @@
 """The tile fa_fwd picks on its own (fa_launch_cfg): 8-wavefront tiles when the
-grid fills the GPU, 4-wavefront tiles when it would not, one-wavefront tiles at
-d = 64 and 128 when even those would not; on non-causal grids that fill the GPU,
-the 8-, 12- or 4-wavefront tile that leaves the busiest compute unit the least
-work; and the default launch is bit-identical to the explicit launch of the
-configuration it names."""
+grid fills the GPU; when it would not, at d = 64 and 128 the key-split tile
+(four wavefronts sharing each 32-query block) if causal or if 4-wavefront tiles
+too would leave compute units idle, else 4-wavefront tiles; on non-causal grids
+that fill the GPU, the 8-, 12- or 4-wavefront tile that leaves the busiest
+compute unit the least work; and the default launch is bit-identical to the
+explicit launch of the configuration it names."""
 import numpy as np
 import pytest
 
@@ -27,18 +28,26 @@ def test_choice_follows_the_grid():
     import torch
     import flashattention_forward_fa2_amd as fa
     cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ks = (1, 4, 32, 4)
     assert fa.launch_cfg(4, 8, 4096, 64, False) == (1, 8, 64)          # 512 workgroups of 256 queries
     assert fa.launch_cfg(1, 8, 4096, 64, False) == (1, 4, 64)          # 128 of them; 256 of 128 queries
-    assert fa.launch_cfg(1, 8, 1024, 64, True) == (1, 1, 64)           # 32, then 64: fewer than the CUs
-    assert fa.launch_cfg(1, 8, 1024, 64, False, "f16") == (1, 1, 64)
-    assert fa.launch_cfg(1, 1, 256, 64, False) == (1, 1, 64)
-    assert fa.launch_cfg(1, 8, 1024, 128, False, "f16") == (1, 1, 32)  # d = 128: 32-key one-wave tiles
-    assert fa.launch_cfg(1, 8, 4096, 128, True) == (1, 4, 64)
+    assert fa.launch_cfg(1, 8, 4096, 64, True) == ks                   # causal: key split below the CU count
+    assert fa.launch_cfg(1, 8, 4096, 128, True) == ks
+    assert fa.launch_cfg(1, 8, 1024, 64, True) == ks                   # 32, then 64: fewer than the CUs
+    assert fa.launch_cfg(1, 8, 1024, 64, False, "f16") == ks
+    assert fa.launch_cfg(1, 1, 256, 64, False) == ks
+    assert fa.launch_cfg(1, 8, 1024, 128, False, "f16") == ks
+    assert fa.launch_cfg(1, 8, 1024, 32, False) == (1, 4, 64)          # d = 32: no key-split tile
     assert fa.launch_cfg(1, 8, 1024, 256, False) == (1, 4, 32)         # d = 256 has the 4-wave tile only
     assert fa.launch_cfg(1, 8, 1024, 64, False, "f32") == (1, 4, 32)
     n = 256 * ((cus + 7) // 8)                                         # 8 heads x n/256 tiles >= cus
     assert fa.launch_cfg(1, 8, n, 64, False) == (1, 8, 64)
+    assert fa.launch_cfg(1, 8, n, 64, True) == (1, 8, 64)
     assert fa.launch_cfg(1, 8, n - 256, 64, False) == (1, 4, 64)      # 8 * (ceil(cus / 8) - 1) < cus
+    assert fa.launch_cfg(1, 8, n - 256, 64, True) == ks
+    m = 128 * ((cus + 7) // 8)                                         # 4-wave grid just fills the CUs
+    assert fa.launch_cfg(1, 8, m, 64, False) == (1, 4, 64)
+    assert fa.launch_cfg(1, 8, m - 128, 64, False) == ks
 
 
 def balanced(B, H, N, waves, permille, cus):

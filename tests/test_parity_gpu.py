@@ -67,7 +67,7 @@ def all_variants():
         return []
 
 
-@pytest.mark.parametrize("variant", all_variants(), ids=lambda v: "d%d-c%d-qb%d-w%d-bk%d" % (v[0], v[1], *v[2]))
+@pytest.mark.parametrize("variant", all_variants(), ids=lambda v: "d%d-c%d-%s" % (v[0], v[1], "-".join(map(str, v[2]))))
 def test_every_compiled_variant(variant):
     d, causal, cfg = variant
     q, k, v = random_qkv(77, 2, 3, 600, d, sigma_qk=2.0)
