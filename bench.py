@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--cfg", type=str, default=None, help="force a tile variant: qb,waves,bk")
+    ap.add_argument("--cfg", type=str, default=None, help="force a tile variant: qb,waves,bk[,ksplit]")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows-per-head", type=int, default=None)
     ap.add_argument("--ramp-seconds", type=float, default=1.0,
