@@ -590,15 +590,21 @@ __global__ __launch_bounds__(S * 64) void fa_fwd_wsplit_kernel(const Params pr) 
   __shared__ __attribute__((aligned(1024))) char lds1[S * kStage];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, lr = lane & 31;
-  // Causal: the longest query blocks first (one per head, then the next).
+  // Causal: the longest query blocks first, one per head and then the next, so
+  // with B*H a multiple of 8 each head's blocks land on one XCD (workgroups are
+  // dealt round-robin over the 8 XCDs).  Non-causal: head-major, with ids
+  // remapped as in fa_fwd_kernel so that each XCD works through a contiguous
+  // set of heads and one L2 fetches a head's K and V.
   const int nqt = pr.nqt;
   int bh, qt;
   if (CAUSAL) {
     bh = (int)(blockIdx.x % BH);
     qt = nqt - 1 - (int)(blockIdx.x / BH);
   } else {
-    bh = (int)(blockIdx.x / nqt);
-    qt = (int)(blockIdx.x % nqt);
+    const int i = (int)blockIdx.x, total = (int)gridDim.x;
+    const int t = (BH % 8) == 0 ? (i & 7) * (total >> 3) + (i >> 3) : i;
+    bh = t / nqt;
+    qt = t - bh * nqt;
   }
   const int batch = bh / pr.H, hd = bh - batch * pr.H;
   const long long q_off = STRIDED ? batch * pr.q_sb + hd * pr.q_sh : (long long)bh * Nq * D;
