@@ -40,7 +40,7 @@ def run(q, k, v, d, causal, dtype="bf16", bnhd=False, cfg=KS):
     tq, tk, tv = (to_device(a, dtype=dtype) for a in (q, k, v))
     if bnhd:  # stored [B, N, H, d]; the kernel sees [B, H, N, d] views with row stride H*d
         tq, tk, tv = (t.permute(0, 2, 1, 3).contiguous().transpose(1, 2) for t in (tq, tk, tv))
-    out, lse = fa.fa_fwd_ex(tq, tk, tv, scale=fp32_scale(d), causal=causal, cfg=cfg)
+    out, lse = fa.fa_fwd_ex(tq, tk, tv, scale=fp32_scale(d), causal=causal, cfg=cfg)  # cfg None: the default
     torch.cuda.synchronize()
     return out, lse
 
@@ -104,3 +104,18 @@ def test_default_short_workload_uses_the_tile(causal):
     o2, l2 = fa.fa_fwd(q, k, v, scale=fp32_scale(d), causal=bool(causal), cfg=fa.launch_cfg(B, H, N, d, bool(causal)))
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_long_key_range(d):
+    """100 queries over 2^20 + 17 keys (the default tile on this small grid):
+    each wavefront sweeps 8192 key tiles, whose byte offsets inside the head
+    reach 2^28 (d = 128), the last tile ragged; every row, both masks (causal
+    top-left: query i sees keys 0..i only)."""
+    import flashattention_forward_fa2_amd as fa
+    Nq, Nk = 100, (1 << 20) + 17
+    assert fa.launch_cfg(1, 1, Nq, d, False) == KS and fa.launch_cfg(1, 1, Nq, d, True) == KS
+    q, _, _ = random_qkv(8600 + d, 1, 1, Nq, d)
+    _, k, v = random_qkv(8700 + d, 1, 1, Nk, d)
+    for causal in (0, 1):
+        check(q, k, v, d, causal, "key split long Nk=%d d=%d causal=%d" % (Nk, d, causal), cfg=None)
