@@ -128,8 +128,8 @@ hipError_t run_merge(const fa::Params& p, int d, int dtype, hipStream_t s) {
   {D, C, 1, W, BK, FA_DTYPE_F32, &launch_f32<D, (C) != 0, W, BK, false>, &launch_f32<D, (C) != 0, W, BK, true>, \
    nullptr}
 // The key-split tile (1, 4, 32) with ksplit 4: four wavefronts per 32-query
-// block, 32-key tiles in a ring per wavefront (64 KB of LDS at d = 64, 128 KB at
-// d = 128); no split-path launcher.
+// block, 32-key tiles in a ring per wavefront (32 KB of LDS at d = 32, 64 KB at
+// d = 64, 128 KB at d = 128); no split-path launcher.
 #define FA_VARIANT_KS(D, C, T, DT)                                                                     \
   {D, C, 1, 4, 32, DT, &launch_wsplit<D, (C) != 0, 4, 32, false, T>, &launch_wsplit<D, (C) != 0, 4, 32, true, T>, \
    nullptr, 4}
@@ -157,7 +157,8 @@ const Variant kVariants[] = {
     FA_VARIANT16(128, 0, 1, 1, 32), FA_VARIANT16(128, 1, 1, 1, 32),
     FA_VARIANT32(64, 0, 4, 32), FA_VARIANT32(64, 1, 4, 32), FA_VARIANT32(128, 0, 4, 32),
     FA_VARIANT32(128, 1, 4, 32),
-    FA_VARIANTS_KS(64, 0), FA_VARIANTS_KS(64, 1), FA_VARIANTS_KS(128, 0), FA_VARIANTS_KS(128, 1),
+    FA_VARIANTS_KS(32, 0), FA_VARIANTS_KS(32, 1), FA_VARIANTS_KS(64, 0), FA_VARIANTS_KS(64, 1),
+    FA_VARIANTS_KS(128, 0), FA_VARIANTS_KS(128, 1),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -237,8 +238,8 @@ int device_cus() {
 // The tile a launch uses when the caller names none: default_cfg_dt, except
 // on grids that would leave compute units idle or unevenly loaded.
 // * An 8-wavefront grid (B*H*ceil(Nq/256) workgroups, one per CU at a time)
-//   with fewer workgroups than compute units: at d = 64 and 128 (bf16, fp16)
-//   the key-split tile (1, 4, 32, ksplit 4: four wavefronts share each block of
+//   with fewer workgroups than compute units: at d = 32, 64 and 128 (bf16,
+//   fp16) the key-split tile (1, 4, 32, ksplit 4: four wavefronts share each block of
 //   32 queries and split its keys) when causal, or when the 4-wavefront grid
 //   too leaves compute units idle; otherwise 4-wavefront tiles, which double
 //   the workgroups (and, where no key-split tile is compiled, one-wavefront

@@ -219,10 +219,11 @@ int fa_default_cfg(int N, int d, int causal, fa_tile_cfg *cfg);
 /* The configuration fa_fwd and fa_fwd_ex pick for these sizes and element type
  * on the current device: fa_default_cfg's, except that when its 8-wavefront
  * grid (B*H*ceil(Nq/256) workgroups) is smaller than the device's compute-unit
- * count: at d = 64 or 128 (bf16 or fp16) the key-split tile (1, 4, 32, ksplit
- * 4) if causal, or if the 4-wavefront grid (B*H*ceil(Nq/128)) is smaller too;
- * else the 4-wavefront tile (1, 4, 64), which doubles the workgroups (at d = 32
- * and 256, and fp32, where no key-split tile is compiled).  Non-causal
+ * count: at d = 32, 64 or 128 (bf16 or fp16) the key-split tile (1, 4, 32,
+ * ksplit 4) if causal, or if the 4-wavefront grid (B*H*ceil(Nq/128)) is smaller
+ * too; else the 4-wavefront tile (1, 4, 64), which doubles the workgroups (d =
+ * 256 and fp32 keep their 4-wavefront defaults: no key-split tile is compiled
+ * for them).  Non-causal
  * launches at d = 32, 64 or 128 (bf16 or fp16) whose 8-wavefront grid fills
  * the device take, of (1, 8, 64), (1, 12, 64) (d = 64 only) and (1, 4, 64),
  * the tile that leaves the busiest compute unit the least work:

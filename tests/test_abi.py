@@ -152,23 +152,24 @@ def test_tile_cfg_layout_matches_the_header(tmp_path):
 
 
 def test_key_split_variants(lib):
-    """The key-split tile (1, 4, 32, ksplit 4) is compiled at d = 64 and 128 for
-    bf16 and fp16, both masks; other key-split shapes, and d = 32, are refused
-    before any device call (FA_ERR_ARG), while a compiled one gets as far as the
-    device check."""
+    """The key-split tile (1, 4, 32, ksplit 4) is compiled at d = 32, 64 and 128
+    for bf16 and fp16, both masks; other key-split shapes, and d = 256, are
+    refused before any device call (FA_ERR_ARG), while a compiled one gets as far
+    as the device check."""
     for dtype in ("bf16", "f16"):
         vs = fa.variants(dtype)
-        for d in (64, 128):
+        for d in (32, 64, 128):
             for causal in (0, 1):
                 assert (d, causal, (1, 4, 32, 4)) in vs
-        assert not any(len(v[2]) == 4 for v in vs if v[0] in (32, 256))
+        assert not any(len(v[2]) == 4 for v in vs if v[0] == 256)
     assert not any(len(v[2]) == 4 for v in fa.variants("f32"))
-    assert call(d=32, cfg=(1, 4, 32, 4)) == 5
+    assert call(d=256, cfg=(1, 4, 32, 4)) == 5
     assert call(d=64, cfg=(1, 4, 32, 3)) == 5
     assert call(d=64, cfg=(1, 4, 64, 4)) == 5
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         assert call(d=64, cfg=(1, 4, 32, 4)) == 8
+        assert call(d=32, cfg=(1, 4, 32, 4)) == 8
         assert call(d=128, causal=1, cfg=(1, 4, 32, 4)) == 8
     assert call(d=64, cfg=(1, 4, 32, 0)) == call(d=64, cfg=(1, 4, 32))  # ksplit 0 is ksplit 1
 

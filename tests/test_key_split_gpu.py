@@ -53,7 +53,7 @@ def check(q, k, v, d, causal, label, dtype="bf16", **kw):
     return out, lse
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [0, 1])
 @pytest.mark.parametrize("Nq,Nk", [(1, 1), (5, 40), (40, 5), (33, 97), (200, 64), (64, 200), (300, 1000),
                                    (1000, 300), (257, 257)])
@@ -65,7 +65,7 @@ def test_lengths(Nq, Nk, d, causal):
     check(q, k, v, d, causal, "key split Nq=%d Nk=%d d=%d causal=%d" % (Nq, Nk, d, causal))
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [0, 1])
 def test_peaked_scores(d, causal):
     """Q, K ~ N(0, 4^2): each wavefront's reference maximum moves often and the
@@ -76,7 +76,7 @@ def test_peaked_scores(d, causal):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 def test_strided_and_fp16(d, dtype):
     """[B, N, H, d] views (the strided instantiation) in bf16 and fp16, both masks,
     and bit-identity with the contiguous launch of the same tile."""

@@ -1,5 +1,5 @@
 """The tile fa_fwd picks on its own (fa_launch_cfg): 8-wavefront tiles when the
-grid fills the GPU; when it would not, at d = 64 and 128 the key-split tile
+grid fills the GPU; when it would not, at d = 32, 64 and 128 the key-split tile
 (four wavefronts sharing each 32-query block) if causal or if 4-wavefront tiles
 too would leave compute units idle, else 4-wavefront tiles; on non-causal grids
 that fill the GPU, the 8-, 12- or 4-wavefront tile that leaves the busiest
@@ -37,7 +37,8 @@ def test_choice_follows_the_grid():
     assert fa.launch_cfg(1, 8, 1024, 64, False, "f16") == ks
     assert fa.launch_cfg(1, 1, 256, 64, False) == ks
     assert fa.launch_cfg(1, 8, 1024, 128, False, "f16") == ks
-    assert fa.launch_cfg(1, 8, 1024, 32, False) == (1, 4, 64)          # d = 32: no key-split tile
+    assert fa.launch_cfg(1, 8, 1024, 32, False) == ks
+    assert fa.launch_cfg(1, 8, 4096, 32, False) == (1, 4, 64)          # the 4-wave grid fills the CUs
     assert fa.launch_cfg(1, 8, 1024, 256, False) == (1, 4, 32)         # d = 256 has the 4-wave tile only
     assert fa.launch_cfg(1, 8, 1024, 64, False, "f32") == (1, 4, 32)
     n = 256 * ((cus + 7) // 8)                                         # 8 heads x n/256 tiles >= cus
