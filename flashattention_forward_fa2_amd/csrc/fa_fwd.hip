@@ -69,15 +69,16 @@ hipError_t launch_variant(const fa::Params& p, int B, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Key split inside the workgroup: S wavefronts share each block of 32 queries.
-template <int D, bool CAUSAL, int S, int BK, bool STRIDED, typename E>
+// Key split inside the workgroup: S wavefronts share each block of 32 queries
+// (SPLIT: one workgroup per key split as well, p.nsplit of them).
+template <int D, bool CAUSAL, int S, int BK, bool STRIDED, typename E, bool SPLIT = false>
 hipError_t launch_wsplit(const fa::Params& p, int B, hipStream_t stream) {
   fa::Params pr = p;
   pr.nqt = (p.Nq + 31) / 32;
-  const long long blocks = (long long)B * p.H * pr.nqt;
+  const long long blocks = (long long)B * p.H * pr.nqt * (SPLIT ? p.nsplit : 1);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fa::fa_fwd_wsplit_kernel<D, CAUSAL, S, BK, STRIDED, E>), dim3((unsigned)blocks), dim3(S * 64), 0,
-                     stream, pr);
+  hipLaunchKernelGGL((fa::fa_fwd_wsplit_kernel<D, CAUSAL, S, BK, STRIDED, E, SPLIT>), dim3((unsigned)blocks),
+                     dim3(S * 64), 0, stream, pr);
   return hipGetLastError();
 }
 
@@ -129,10 +130,10 @@ hipError_t run_merge(const fa::Params& p, int d, int dtype, hipStream_t s) {
    nullptr}
 // The key-split tile (1, 4, 32) with ksplit 4: four wavefronts per 32-query
 // block, 32-key tiles in a ring per wavefront (32 KB of LDS at d = 32, 64 KB at
-// d = 64, 128 KB at d = 128); no split-path launcher.
+// d = 64, 128 KB at d = 128); also the split path's tile for short query ranges.
 #define FA_VARIANT_KS(D, C, T, DT)                                                                     \
   {D, C, 1, 4, 32, DT, &launch_wsplit<D, (C) != 0, 4, 32, false, T>, &launch_wsplit<D, (C) != 0, 4, 32, true, T>, \
-   nullptr, 4}
+   &launch_wsplit<D, (C) != 0, 4, 32, true, T, true>, 4}
 #define FA_VARIANTS_KS(D, C) FA_VARIANT_KS(D, C, fa::Bf16, FA_DTYPE_BF16), FA_VARIANT_KS(D, C, fa::F16, FA_DTYPE_F16)
 #define FA_VARIANTS_DC(D, C) \
   FA_VARIANT(D, C, 1, 4, 64), FA_VARIANT(D, C, 2, 4, 64), FA_VARIANT(D, C, 1, 8, 64)
@@ -405,23 +406,30 @@ long long split_workspace(int B, int H, int Nq, int d, int S_eff) {
 }
 
 // Tile configuration of the split path: short query ranges take smaller
-// workgroups so fewer MFMA rows are padding -- one wavefront of 32 queries when
-// Nq <= 32 (decoding: 32 KB of LDS each, so five fit on a CU and more key
-// streams are in flight), the 4-wave, 128-query tile when Nq <= 128 (d = 32
-// and 256 have the 4-wave tiles only).
+// workgroups so fewer MFMA rows are padding -- the key-split tile when Nq <= 32
+// (decoding: one block of 32 queries whose four wavefronts each stream their
+// own key tiles, so four key streams per split are in flight), the 4-wave,
+// 128-query tile when Nq <= 128 (d = 256 has the 4-wave tiles only).
 fa_tile_cfg split_cfg(int Nq, int Nk, int d, int causal) {
-  if (Nq <= 32 && (d == 64 || d == 128)) return fa_tile_cfg{1, 1, d == 128 ? 32 : 64};
+  if (Nq <= 32 && d != 256) return fa_tile_cfg{1, 4, 32, 4};
   return Nq <= 128 && d != 256 ? fa_tile_cfg{1, 4, 64} : default_cfg(Nk, d, causal);
 }
 
 // (the same for both masks, so the workspace query needs no causal flag)
 int default_splits(int B, int H, int Nq, int Nk, int d) {
   const fa_tile_cfg c = split_cfg(Nq, Nk, d, 0);
-  const long long wgs = (long long)B * H * ((Nq + c.waves * c.qb * 32 - 1) / (c.waves * c.qb * 32));
-  long long s = (512 + wgs - 1) / wgs;       // about 512 workgroups
-  // at least 256 keys per split (512 for single-wavefront workgroups, whose
-  // per-split setup weighs more against their short key streams)
-  s = std::min<long long>(s, std::max(1, Nk / (c.waves == 1 ? 512 : 256)));
+  const int rows = c.ksplit > 1 ? 32 : c.waves * c.qb * 32;  // query rows per workgroup
+  const long long wgs = (long long)B * H * ((Nq + rows - 1) / rows);
+  long long s;
+  if (c.ksplit > 1) {
+    // key-split tile: about 256 workgroups (one per CU at d = 128's 128 KB of
+    // LDS), at least 512 keys per split (four 32-key tiles per wavefront)
+    s = (256 + wgs - 1) / wgs;
+    s = std::min<long long>(s, std::max(1, Nk / 512));
+  } else {
+    s = (512 + wgs - 1) / wgs;  // about 512 workgroups
+    s = std::min<long long>(s, std::max(1, Nk / 256));  // at least 256 keys per split
+  }
   return (int)std::max<long long>(1, std::min<long long>(s, 1024));
 }
 

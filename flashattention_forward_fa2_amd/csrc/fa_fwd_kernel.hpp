@@ -573,7 +573,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // "FlashAttention-2, -3, and what came after", the Flash-Decoding paragraph; the
 // merge of two partial states is that page's online max/sum exercise), done
 // inside one launch instead of two.
-template <int D, bool CAUSAL, int S, int BK, bool STRIDED, typename E = Bf16>
+//
+// SPLIT = true: one workgroup per (split of the keys, head, query block), as
+// fa_fwd_kernel's SPLIT instantiation: keys [s * chunk, min(Nk, (s + 1) *
+// chunk)), partial results O / l (fp32) and LSE (or 0 and -inf for a row that
+// sees none of them) into the caller's workspace for fa_merge_kernel.
+template <int D, bool CAUSAL, int S, int BK, bool STRIDED, typename E = Bf16, bool SPLIT = false>
 __global__ __launch_bounds__(S * 64) void fa_fwd_wsplit_kernel(const Params pr) {
   constexpr int kTileBytes = BK * D * 2;
   constexpr int kBlocks = kTileBytes / 1024;
@@ -596,13 +601,15 @@ __global__ __launch_bounds__(S * 64) void fa_fwd_wsplit_kernel(const Params pr) 
   // remapped as in fa_fwd_kernel so that each XCD works through a contiguous
   // set of heads and one L2 fetches a head's K and V.
   const int nqt = pr.nqt;
+  const int split = SPLIT ? (int)(blockIdx.x % pr.nsplit) : 0;
+  const int bid = SPLIT ? (int)(blockIdx.x / pr.nsplit) : (int)blockIdx.x;
   int bh, qt;
   if (CAUSAL) {
-    bh = (int)(blockIdx.x % BH);
-    qt = nqt - 1 - (int)(blockIdx.x / BH);
+    bh = bid % BH;
+    qt = nqt - 1 - bid / BH;
   } else {
-    const int i = (int)blockIdx.x, total = (int)gridDim.x;
-    const int t = (BH % 8) == 0 ? (i & 7) * (total >> 3) + (i >> 3) : i;
+    const int total = SPLIT ? (int)(gridDim.x / pr.nsplit) : (int)gridDim.x;
+    const int t = (BH % 8) == 0 ? (bid & 7) * (total >> 3) + (bid >> 3) : bid;
     bh = t / nqt;
     qt = t - bh * nqt;
   }
@@ -650,15 +657,19 @@ __global__ __launch_bounds__(S * 64) void fa_fwd_wsplit_kernel(const Params pr) 
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m = -__FLT_MAX__, thr = -__FLT_MAX__, l = 0.f;
 
-  // Keys [0, kend) in tiles of BK; this wavefront's are wave, wave + S, ...
-  const int kend = CAUSAL ? min(q0 + 32, Nk) : Nk;
-  const int ntiles = (kend + BK - 1) / BK;  // >= 1
+  // Keys [kbeg, kend) in tiles of BK (all of them unless split; causal
+  // top-left: none at or after q0 + 32); this wavefront's are tiles wave,
+  // wave + S, ...
+  const int kbeg = SPLIT ? split * pr.chunk : 0;
+  const int klim = SPLIT ? min(Nk, kbeg + pr.chunk) : Nk;
+  const int kend = CAUSAL ? min(q0 + 32, klim) : klim;
+  const int ntiles = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
   const int nmine = ntiles > wave ? (ntiles - 1 - wave) / S + 1 : 0;
   char* const st0 = lds0 + wave * kStage;
   char* const st1 = lds1 + wave * kStage;
 
   auto issue = [&](int j, char* dst) {
-    const uint32_t gk = (uint32_t)(j * BK) * k_rs * 2, gv = (uint32_t)(j * BK) * v_rs * 2;
+    const uint32_t gk = (uint32_t)(kbeg + j * BK) * k_rs * 2, gv = (uint32_t)(kbeg + j * BK) * v_rs * 2;
 #pragma unroll
     for (int b = 0; b < kBlocks; ++b) {
       dma16(krs, dst + b * 1024, dma_k[b] + gk);
@@ -694,7 +705,7 @@ __global__ __launch_bounds__(S * 64) void fa_fwd_wsplit_kernel(const Params pr) 
       }
     if (masked) {
       const int base = k0 + 4 * g;
-      const int lim = CAUSAL ? min(q0 + lr + 1, Nk) - base : Nk - base;
+      const int lim = CAUSAL ? min(q0 + lr + 1, klim) - base : klim - base;
 #pragma unroll
       for (int kb = 0; kb < BK / 32; ++kb)
 #pragma unroll
@@ -746,8 +757,8 @@ __global__ __launch_bounds__(S * 64) void fa_fwd_wsplit_kernel(const Params pr) 
   auto step = [&](int i, char* cur, char* nxt) {
     const int j = wave + i * S;
     if (i + 1 < nmine) issue(j + S, nxt);
-    const int k0 = j * BK;
-    const bool masked = (CAUSAL && (k0 + BK - 1 > q0)) || (k0 + BK > Nk);
+    const int k0 = kbeg + j * BK;
+    const bool masked = (CAUSAL && (k0 + BK - 1 > q0)) || (k0 + BK > klim);
     compute_tile(cur, k0, masked);
     wait_vmcnt<0>();
   };
@@ -795,20 +806,37 @@ __global__ __launch_bounds__(S * 64) void fa_fwd_wsplit_kernel(const Params pr) 
     wt[p] = __builtin_amdgcn_exp2f(pm[p * 32 + lr] - M);
     L += wt[p] * pl[p * 32 + lr];
   }
-  const float inv = 1.0f / L;
   const int query = q0 + lr;
   constexpr int CPL = D / S / 2;  // columns per lane
   static_assert(CPL % 4 == 0, "columns per lane");
+  const int c0 = wave * (D / S) + g * CPL;
+  auto column = [&](int c) {  // columns c0 + c .. c0 + c + 3 of this row, unnormalised
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < S; ++p)
+      acc += wt[p] * *reinterpret_cast<const f32x4*>(po + (p * 32 + lr) * D + ((((c0 + c) >> 2) ^ (lr & 7)) << 2));
+    return acc;
+  };
+  if constexpr (SPLIT) {
+    // A row that sees none of this split's keys has L = 0: O = 0, LSE = -inf.
+    const bool none = !(L > 0.f);
+    const float inv = none ? 0.f : 1.0f / L;
+    if (query < Nq) {
+      const long long row = ((long long)split * BH + bh) * Nq + query;
+      float* orow = pr.part_o + row * D;
+#pragma unroll
+      for (int c = 0; c < CPL; c += 4) *reinterpret_cast<f32x4*>(orow + c0 + c) = column(c) * inv;
+      if (wave == 0 && g == 0) pr.part_lse[row] = none ? -__builtin_inff() : (M + log2f(L)) * kLn2;
+    }
+    return;
+  }
+  const float inv = 1.0f / L;
   if (query < Nq) {
     const long long o_off = STRIDED ? batch * pr.o_sb + hd * pr.o_sh : (long long)bh * Nq * D;
     uint16_t* orow = pr.out + o_off + (long long)query * o_rs;
-    const int c0 = wave * (D / S) + g * CPL;
 #pragma unroll
     for (int c = 0; c < CPL; c += 4) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int p = 0; p < S; ++p)
-        acc += wt[p] * *reinterpret_cast<const f32x4*>(po + (p * 32 + lr) * D + ((((c0 + c) >> 2) ^ (lr & 7)) << 2));
+      const f32x4 acc = column(c);
       u32x2 w;
       w[0] = E::pack(acc[0] * inv, acc[1] * inv);
       w[1] = E::pack(acc[2] * inv, acc[3] * inv);

@@ -207,9 +207,12 @@ int fa_fwd_splitkv_noalloc(const fa_fwd_desc *desc, int num_splits);
 /* Workspace bytes for fa_fwd_splitkv (>= 0), or minus an error code. */
 long long fa_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);
 
-/* The split count fa_fwd_splitkv uses for num_splits = 0 (>= 1; about two
- * workgroups per compute unit, at least 256 keys per split), or minus an error code.
- * (The split path runs 128-query workgroups when Nq <= 128, else fa_fwd's tile.) */
+/* The split count fa_fwd_splitkv uses for num_splits = 0 (>= 1), or minus an
+ * error code.  The split path runs the key-split tile (one block of 32 queries,
+ * four wavefronts splitting each split's keys again) when Nq <= 32 and d <= 128,
+ * with about 256 workgroups and at least 512 keys per split; 128-query
+ * workgroups when Nq <= 128 (d <= 128), else fa_fwd's tile, with about 512
+ * workgroups and at least 256 keys per split. */
 int fa_splitkv_default_splits(int B, int H, int Nq, int Nk, int d, int causal);
 
 /* The configuration for (N, d, causal) on a grid that gives every compute unit

@@ -253,9 +253,12 @@ def test_splitkv_workspace_and_default_splits(lib):
     # 16 requested over 100 keys: chunk 64, 2 splits used
     assert fa.splitkv_workspace_bytes(1, 1, 1, 100, 64, 16) == 2 * 65 * 4
     assert fa.splitkv_default_splits(1, 8, 1024, 1024, 64) == 4      # 32 workgroups, >= 256 keys per split
-    assert fa.splitkv_default_splits(1, 32, 1, 32768, 128) == 16     # decode: 32 workgroups -> 16 splits
-    assert fa.splitkv_default_splits(4, 32, 1, 8192, 128) == 4       # 128 single-wavefront workgroups
-    assert fa.splitkv_default_splits(4, 8, 1, 4096, 64) == 8         # >= 512 keys per single-wave split
+    # decoding (Nq <= 32): key-split workgroups of one 32-query block, about 256 of them
+    assert fa.splitkv_default_splits(1, 32, 1, 32768, 128) == 8      # 32 workgroups -> 8 splits
+    assert fa.splitkv_default_splits(4, 32, 1, 8192, 128) == 2       # 128 workgroups -> 2 splits
+    assert fa.splitkv_default_splits(8, 32, 1, 4096, 128) == 1       # 256 workgroups already
+    assert fa.splitkv_default_splits(4, 8, 1, 4096, 64) == 8         # 32 workgroups, 512 keys per split
+    assert fa.splitkv_default_splits(1, 1, 1, 1000, 64) == 1         # >= 512 keys per split
     assert fa.splitkv_default_splits(4, 8, 4096, 4096, 64) == 1      # 512 workgroups already
     with pytest.raises(fa.FaError):
         fa.splitkv_workspace_bytes(1, 1, 1, 1, 96, 1)
