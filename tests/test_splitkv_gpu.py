@@ -37,6 +37,8 @@ def qkv(seed, B, H, Nq, Nk, d):
     (1, 4, 1, 8192, 128, 0, 16), (1, 4, 1, 8192, 128, 1, 16),    # one query over a long key range
     (1, 2, 37, 3000, 64, 1, 5), (2, 2, 300, 777, 128, 1, 3),
     (1, 1, 5, 100, 64, 0, 16),                                    # more splits asked than key tiles
+    (2, 3, 7, 2000, 32, 1, 0), (1, 2, 1, 5000, 32, 0, 0),         # d = 32, default splits
+    (1, 2, 32, 3000, 128, 1, 0),                                  # a full 32-query block, default splits
 ])
 def test_splitkv_matches_oracle(B, H, Nq, Nk, d, causal, S):
     import torch
