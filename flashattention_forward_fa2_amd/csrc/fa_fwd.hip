@@ -11,6 +11,7 @@
 #include <cstring>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "fa_fwd_f32_kernel.hpp"
 #include "fa_fwd_kernel.hpp"
@@ -27,6 +28,7 @@ struct Variant {
   Launcher launch_strided;  // any strides
   Launcher launch_split;    // any strides, one key split per workgroup (p.nsplit splits)
   int ksplit;               // wavefronts splitting one query block's keys (0 or 1: none)
+  int (*resident)();        // fa_fwd_kernel tiles: workgroups of the contiguous kernel per CU
 };
 
 // 0 and 1 both mean "each wavefront owns its own queries".
@@ -122,7 +124,8 @@ hipError_t run_merge(const fa::Params& p, int d, int dtype, hipStream_t s) {
 
 #define FA_VARIANT_T(D, C, QB, W, BK, T, DT)                                                          \
   {D, C, QB, W, BK, DT, &launch_variant<D, (C) != 0, QB, W, BK, false, false, T>,                     \
-   &launch_variant<D, (C) != 0, QB, W, BK, true, false, T>, &launch_variant<D, (C) != 0, QB, W, BK, true, true, T>}
+   &launch_variant<D, (C) != 0, QB, W, BK, true, false, T>, &launch_variant<D, (C) != 0, QB, W, BK, true, true, T>, \
+   0, &resident_per_cu<D, (C) != 0, QB, W, BK, false, false, T>}
 #define FA_VARIANT(D, C, QB, W, BK) FA_VARIANT_T(D, C, QB, W, BK, fa::Bf16, FA_DTYPE_BF16)
 #define FA_VARIANT16(D, C, QB, W, BK) FA_VARIANT_T(D, C, QB, W, BK, fa::F16, FA_DTYPE_F16)
 #define FA_VARIANT32(D, C, W, BK)                                                                        \
@@ -236,47 +239,99 @@ int device_cus() {
   return check_device(&cus) == FA_OK ? cus : 0;
 }
 
-// The tile a launch uses when the caller names none: default_cfg_dt, except
-// on grids that would leave compute units idle or unevenly loaded.
-// * An 8-wavefront grid (B*H*ceil(Nq/256) workgroups, one per CU at a time)
-//   with fewer workgroups than compute units: at d = 32, 64 and 128 (bf16,
-//   fp16) the key-split tile (1, 4, 32, ksplit 4: four wavefronts share each block of
-//   32 queries and split its keys) when causal, or when the 4-wavefront grid
-//   too leaves compute units idle; otherwise 4-wavefront tiles, which double
-//   the workgroups (and, where no key-split tile is compiled, one-wavefront
-//   tiles when those still leave compute units idle).  Causal work is uneven
-//   across query blocks, and the key split evens it inside each workgroup.
-// * Non-causal grids at d = 32, 64 and 128 that fill the GPU: every query tile
-//   costs the same, so a launch lasts about as long as the busiest CU, which
-//   runs ceil(workgroups / CUs) tiles of `waves` wavefronts each.  Of the
-//   8-, 12- (d = 64) and 4-wavefront tiles the one with the least such work
-//   is taken, each weighed by its measured speed on grids that divide evenly
-//   (per mille of the 8-wavefront tile's time: 12 waves 975, 4 waves 1025 at
-//   d = 32, 1030 at d = 64 and 1050 at d = 128); ties keep the 8-wavefront tile.
+// How evenly a causal launch of fa_fwd_kernel with `rows`-query tiles loads the
+// compute units: the launch order (causal_order) replayed on one XCD (on each
+// when the heads do not split evenly over the 8 XCDs), the first `res` layers
+// of its workgroups placed round-robin over the XCD's CUs as the order assumes
+// and every later one on the CU with the least work so far; a workgroup's work
+// is the number of 64-key tiles it visits.  Returns the mean over the largest
+// per-CU work (1: even), the smallest over the XCDs.
+double causal_balance(int BH, int Nq, int rows, int res, int cus) {
+  const int nqt = (Nq + rows - 1) / rows;
+  const long long total = (long long)BH * nqt;
+  const int cpx = std::max(1, cus / 8);
+  const int xcds = ((BH % 8) == 0 && (cus % 8) == 0) ? 1 : 8;  // one XCD stands for all when they match
+  std::vector<double> work(cpx);
+  double worst = 1.0;
+  for (int x = 0; x < xcds; ++x) {
+    std::fill(work.begin(), work.end(), 0.0);
+    long long k = 0;
+    for (long long i = x; i < total; i += 8, ++k) {
+      int bh, qt;
+      fa::causal_order((int)i, (int)total, BH, nqt, res, cus, bh, qt);
+      const double w = (double)((std::min(qt * rows + rows, Nq) + 63) / 64);
+      const long long c = k < (long long)cpx * res ? k % cpx : std::min_element(work.begin(), work.end()) - work.begin();
+      work[c] += w;
+    }
+    double sum = 0.0, mx = 0.0;
+    for (double v : work) sum += v, mx = std::max(mx, v);
+    if (mx > 0.0) worst = std::min(worst, sum / cpx / mx);
+  }
+  return worst;
+}
+
+// The tile a launch uses when the caller names none: default_cfg_dt (one tile
+// at d = 256 and for fp32), and at d = 32, 64 and 128 (bf16, fp16) a choice by
+// grid size, from tile sweeps on MI355X.  With w8 = B*H*ceil(Nq/256) workgroups
+// of the 8-wavefront tile (one per CU at a time) and w4 = B*H*ceil(Nq/128) of
+// the 4-wavefront tile (1, 4, 64):
+// * Non-causal: the key-split tile (1, 4, 32, ksplit 4: four wavefronts share
+//   each block of 32 queries and split its keys) while 2*w4 <= CUs; (1, 4, 64)
+//   while w4 <= CUs; beyond, every query tile costs the same, so a launch lasts
+//   about as long as the busiest CU, which runs ceil(workgroups / CUs) tiles of
+//   `waves` wavefronts each: of the 8-, 12- (d = 64) and 4-wavefront tiles the
+//   one with the least such work, each weighed by its measured speed on grids
+//   that divide evenly (per mille of the 8-wavefront tile's time: 12 waves 975,
+//   4 waves 1025 at d = 32, 1030 at d = 64 and 1050 at d = 128); ties keep the
+//   8-wavefront tile.
+// * Causal: work per query tile grows along the diagonal.  The key-split tile
+//   while w8 < CUs (at d = 128 only while w4 <= CUs: its 128 KB of LDS leave one
+//   workgroup per CU; at d = 32, with 32 KB, up to w8 <= 1.5 CUs); (1, 8, 64)
+//   from 4 layers of CUs on; in between (1, 8, 64)
+//   where its launch order loads the CUs evenly (causal_balance >= 0.97, e.g.
+//   two layers of tiles paired long with short), else (1, 4, 64), whose smaller
+//   tiles and several workgroups per CU even out what one 256-query tile per CU
+//   cannot -- unless its own order balances worse.
 fa_tile_cfg launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, int cus) {
-  fa_tile_cfg c = default_cfg_dt(Nq, d, causal, dtype);
+  const fa_tile_cfg c = default_cfg_dt(Nq, d, causal, dtype);
+  if (c.waves != 8 || cus <= 0) return c;
+  const fa_tile_cfg ks{1, 4, 32, 4}, four{1, 4, 64};
   auto wgs = [&](const fa_tile_cfg& t) {
     return (long long)B * H * ((Nq + t.qb * t.waves * 32 - 1) / (t.qb * t.waves * 32));
   };
-  if (c.waves == 8 && wgs(c) < cus) {
-    const fa_tile_cfg ks{1, 4, 32, 4};
-    if ((causal || wgs(fa_tile_cfg{1, 4, 64}) < cus) && find_variant(d, causal, ks, dtype)) return ks;
-    c = fa_tile_cfg{1, 4, 64};
-    const fa_tile_cfg one{1, 1, d == 128 ? 32 : 64};
-    if ((d == 64 || d == 128) && wgs(c) < cus && find_variant(d, causal, one, dtype)) c = one;
-    return c;
-  }
-  if (c.waves == 8 && !causal && (d == 32 || d == 64 || d == 128) && cus > 0) {
+  const long long w8 = wgs(c), w4 = wgs(four);
+  const bool has_ks = find_variant(d, causal, ks, dtype) != nullptr;
+  const Variant* v4 = find_variant(d, causal, four, dtype);
+  if (!causal) {
+    if (2 * w4 <= cus && has_ks) return ks;
+    if (w4 <= cus && v4) return four;
     struct Option { fa_tile_cfg t; long long permille; };
     const Option opts[] = {{{1, 8, 64}, 1000}, {{1, 12, 64}, 975}, {{1, 4, 64}, d == 32 ? 1025 : d == 64 ? 1030 : 1050}};
-    long long best = -1;
+    fa_tile_cfg best = c;
+    long long best_cost = -1;
     for (const Option& o : opts) {
       if (!find_variant(d, causal, o.t, dtype)) continue;
       const long long cost = (wgs(o.t) + cus - 1) / cus * o.t.waves * o.permille;
-      if (best < 0 || cost < best) best = cost, c = o.t;
+      if (best_cost < 0 || cost < best_cost) best_cost = cost, best = o.t;
     }
+    return best;
   }
-  return c;
+  if (w8 >= 4LL * cus || !v4) return c;
+  if (has_ks && (w8 < cus ? d <= 64 || w4 <= cus : d == 32 && 2 * w8 <= 3LL * cus)) return ks;
+  // The balance replay costs a few microseconds; remember the last answers.
+  struct Memo { long long bh; int nq, d, dtype, cus; fa_tile_cfg cfg; };
+  thread_local Memo memo[8];
+  thread_local int memo_next = 0;
+  const long long BH = (long long)B * H;
+  for (const Memo& m : memo)
+    if (m.bh == BH && m.nq == Nq && m.d == d && m.dtype == dtype && m.cus == cus) return m.cfg;
+  auto res = [](const Variant* v) { return v && v->resident ? v->resident() : 1; };
+  fa_tile_cfg pick = four;
+  const double b8 = w8 >= cus ? causal_balance((int)BH, Nq, 256, res(find_variant(d, causal, c, dtype)), cus) : 0.0;
+  if (b8 >= 0.97 || causal_balance((int)BH, Nq, 128, res(v4), cus) < b8) pick = c;
+  memo[memo_next] = Memo{BH, Nq, d, dtype, cus, pick};
+  memo_next = (memo_next + 1) % 8;
+  return pick;
 }
 
 // Byte extent of a strided [B, H, N, d] tensor: from its base to one past its

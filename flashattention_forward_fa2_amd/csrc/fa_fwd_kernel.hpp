@@ -201,6 +201,47 @@ struct Params {
   int resident, cus;
 };
 
+// Causal launch order of fa_fwd_kernel: workgroup i of total = BH * nqt ->
+// head bh and query tile qt.  Workgroups are dispatched round-robin over the 8
+// XCDs; when the head count allows, ids are remapped so that each XCD works
+// through a contiguous set of heads (their K/V stay in that XCD's L2).  Tiles
+// run longest first within groups of FA_CAUSAL_GROUP heads of an XCD, one group
+// after the other: a group's lengths n, n, n-1, n-1, ... and the next group's in
+// the same order fill the compute units evenly (a unit freed by a tile of
+// length i takes the next of length n + 1 - i), while only one group's K/V are
+// live at the start of the group.  When res > 1 workgroups fit on a CU, the
+// first res layers of cus workgroups start together and workgroups b and b + cus
+// share a CU; every odd full layer then runs in reverse order, so a long tile
+// shares its CU with a short one instead of one of the same length.  The host's
+// tile rule replays this order to judge how evenly a launch loads the CUs.
+__host__ __device__ __forceinline__ void causal_order(int i, int total, int BH, int nqt, int res, int cus, int& bh,
+                                                      int& qt) {
+  const bool xcd = (BH % 8) == 0;
+  const int t = xcd ? (i & 7) * (total >> 3) + (i >> 3) : i;
+  if (xcd) {
+    const int per = total >> 3, hpx = BH >> 3;
+    const int chunk = t / per;
+    int j = t - chunk * per;
+    const int cpx = cus >> 3;  // CUs per XCD
+    if (res > 1 && cpx > 0 && (cus & 7) == 0) {
+      const int l = j / cpx, p = j - l * cpx;
+      if ((l & 1) && l < res && (l + 1) * cpx <= per) j = l * cpx + (cpx - 1 - p);
+    }
+    const int gs = (hpx % FA_CAUSAL_GROUP) == 0 ? FA_CAUSAL_GROUP : hpx;
+    const int grp = j / (gs * nqt), r = j - grp * gs * nqt;
+    bh = chunk * hpx + grp * gs + r % gs;
+    qt = nqt - 1 - r / gs;
+  } else {
+    int u = t;
+    if (res > 1 && cus > 0) {
+      const int l = u / cus, p = u - l * cus;
+      if ((l & 1) && l < res && (l + 1) * cus <= total) u = l * cus + (cus - 1 - p);
+    }
+    bh = u % BH;
+    qt = nqt - 1 - u / BH;
+  }
+}
+
 // STRIDED = false: every tensor is contiguous [B, H, N, d] (lse [B, H, Nq]) and
 // the strides in `pr` are ignored; the addressing then needs fewer registers.
 // SPLIT = true: one key split per workgroup, partial results to the workspace
@@ -228,49 +269,16 @@ __global__ __launch_bounds__(WAVES * 64) void fa_fwd_kernel(const Params pr) {
   const int lr = lane & 31;  // this lane's query column inside a 32-query block
 
   // ---- which (head, query tile) this workgroup owns -------------------------
-  // Workgroups are dispatched round-robin over the 8 XCDs; when the head count
-  // allows, ids are remapped so that each XCD works through a contiguous set of
-  // heads (their K/V stay in that XCD's L2).  Causal tiles run longest first
-  // within groups of FA_CAUSAL_GROUP heads of an XCD, one group after the
-  // other: a group's lengths n, n, n-1, n-1, ... and the next group's in the
-  // same order fill the compute units evenly (a unit freed by a tile of length
-  // i takes the next of length n + 1 - i), while only one group's K/V are live
-  // at the start of the group.
+  // Non-causal: ids remapped so that each XCD takes a contiguous set of heads
+  // when the head count allows; causal: causal_order.
   const int split = SPLIT ? (int)(blockIdx.x % pr.nsplit) : 0;
   const int total = SPLIT ? (int)(gridDim.x / pr.nsplit) : (int)gridDim.x;
   const int i = SPLIT ? (int)(blockIdx.x / pr.nsplit) : (int)blockIdx.x;
-  const bool xcd = (BH % 8) == 0;
-  const int t = xcd ? (i & 7) * (total >> 3) + (i >> 3) : i;
   int bh, qt;
   if (CAUSAL) {
-    // When several workgroups fit on a CU, the first `resident` layers of
-    // `cus` workgroups start together and workgroups b and b + cus share a CU;
-    // every odd full layer then runs in reverse order, so a long tile shares its
-    // CU with a short one instead of one of the same length.
-    const int res = SPLIT ? 1 : pr.resident;
-    if (xcd) {
-      const int per = total >> 3, hpx = BH >> 3;
-      const int chunk = t / per;
-      int j = t - chunk * per;
-      const int cpx = pr.cus >> 3;  // CUs per XCD
-      if (res > 1 && cpx > 0 && (pr.cus & 7) == 0) {
-        const int l = j / cpx, p = j - l * cpx;
-        if ((l & 1) && l < res && (l + 1) * cpx <= per) j = l * cpx + (cpx - 1 - p);
-      }
-      const int gs = (hpx % FA_CAUSAL_GROUP) == 0 ? FA_CAUSAL_GROUP : hpx;
-      const int grp = j / (gs * nqt), r = j - grp * gs * nqt;
-      bh = chunk * hpx + grp * gs + r % gs;
-      qt = nqt - 1 - r / gs;
-    } else {
-      int u = t;
-      if (res > 1 && pr.cus > 0) {
-        const int l = u / pr.cus, p = u - l * pr.cus;
-        if ((l & 1) && l < res && (l + 1) * pr.cus <= total) u = l * pr.cus + (pr.cus - 1 - p);
-      }
-      bh = u % BH;
-      qt = nqt - 1 - u / BH;
-    }
+    causal_order(i, total, BH, nqt, SPLIT ? 1 : pr.resident, pr.cus, bh, qt);
   } else {
+    const int t = (BH % 8) == 0 ? (i & 7) * (total >> 3) + (i >> 3) : i;
     bh = t / nqt;
     qt = t - bh * nqt;
   }

@@ -220,19 +220,21 @@ int fa_splitkv_default_splits(int B, int H, int Nq, int Nk, int d, int causal);
 int fa_default_cfg(int N, int d, int causal, fa_tile_cfg *cfg);
 
 /* The configuration fa_fwd and fa_fwd_ex pick for these sizes and element type
- * on the current device: fa_default_cfg's, except that when its 8-wavefront
- * grid (B*H*ceil(Nq/256) workgroups) is smaller than the device's compute-unit
- * count: at d = 32, 64 or 128 (bf16 or fp16) the key-split tile (1, 4, 32,
- * ksplit 4) if causal, or if the 4-wavefront grid (B*H*ceil(Nq/128)) is smaller
- * too; else the 4-wavefront tile (1, 4, 64), which doubles the workgroups (d =
- * 256 and fp32 keep their 4-wavefront defaults: no key-split tile is compiled
- * for them).  Non-causal
- * launches at d = 32, 64 or 128 (bf16 or fp16) whose 8-wavefront grid fills
- * the device take, of (1, 8, 64), (1, 12, 64) (d = 64 only) and (1, 4, 64),
- * the tile that leaves the busiest compute unit the least work:
- * ceil(workgroups / CUs) * waves, weighed by the tile's speed on evenly
- * divided grids (8 waves 1.000, 12 waves 0.975, 4 waves 1.025 at d = 32,
- * 1.030 at d = 64 and 1.050 at d = 128); ties keep (1, 8, 64).
+ * on the current device.  d = 256 and fp32 keep fa_default_cfg's 4-wavefront
+ * tile.  At d = 32, 64 or 128 (bf16 or fp16), with w8 = B*H*ceil(Nq/256)
+ * workgroups of (1, 8, 64) and w4 = B*H*ceil(Nq/128) of (1, 4, 64):
+ * - non-causal: the key-split tile (1, 4, 32, ksplit 4) while 2*w4 <= CUs;
+ *   (1, 4, 64) while w4 <= CUs; beyond, of (1, 8, 64), (1, 12, 64) (d = 64
+ *   only) and (1, 4, 64) the tile that leaves the busiest compute unit the
+ *   least work: ceil(workgroups / CUs) * waves, weighed by the tile's speed on
+ *   evenly divided grids (8 waves 1.000, 12 waves 0.975, 4 waves 1.025 at
+ *   d = 32, 1.030 at d = 64 and 1.050 at d = 128); ties keep (1, 8, 64);
+ * - causal: the key-split tile while w8 < CUs (d = 128: while w4 <= CUs;
+ *   d = 32: while w8 <= 1.5 CUs); (1, 8, 64) when w8 >= 4 CUs; in between
+ *   (1, 8, 64) if its launch order, replayed on the host, loads the compute
+ *   units evenly (mean over largest per-CU tile count >= 0.97) or more evenly
+ *   than (1, 4, 64)'s order does, else (1, 4, 64).  The last few answers are
+ *   remembered per host thread.
  * FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_ARG (causal, dtype)
  * or FA_ERR_NO_DEVICE. */
 int fa_launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, fa_tile_cfg *cfg);

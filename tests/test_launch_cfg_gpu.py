@@ -1,10 +1,15 @@
-"""The tile fa_fwd picks on its own (fa_launch_cfg): 8-wavefront tiles when the
-grid fills the GPU; when it would not, at d = 32, 64 and 128 the key-split tile
-(four wavefronts sharing each 32-query block) if causal or if 4-wavefront tiles
-too would leave compute units idle, else 4-wavefront tiles; on non-causal grids
-that fill the GPU, the 8-, 12- or 4-wavefront tile that leaves the busiest
-compute unit the least work; and the default launch is bit-identical to the
-explicit launch of the configuration it names."""
+"""The tile fa_fwd picks on its own (fa_launch_cfg), at d = 32, 64 and 128:
+non-causal, the key-split tile (four wavefronts sharing each 32-query block)
+while twice the 4-wavefront grid fits the compute units, the 4-wavefront tile
+while that grid does, and beyond the 8-, 12- or 4-wavefront tile that leaves the
+busiest compute unit the least work; causal, the key split on grids of fewer
+8-wavefront workgroups than compute units (at d = 128 only while the 4-wavefront
+grid fits them, at d = 32 up to 1.5 times the compute units), the 8-wavefront
+tile from four layers of them on, and in between the 8-wavefront tile only where
+its launch order loads the compute units evenly, else the 4-wavefront one.  The rule is checked against a Python
+restatement of it (its own replay of the causal launch order) and against the
+choices tile sweeps measured on MI355X; the default launch is bit-identical to
+the explicit launch of the configuration it names."""
 import numpy as np
 import pytest
 
@@ -43,12 +48,118 @@ def test_choice_follows_the_grid():
     assert fa.launch_cfg(1, 8, 1024, 64, False, "f32") == (1, 4, 32)
     n = 256 * ((cus + 7) // 8)                                         # 8 heads x n/256 tiles >= cus
     assert fa.launch_cfg(1, 8, n, 64, False) == (1, 8, 64)
-    assert fa.launch_cfg(1, 8, n, 64, True) == (1, 8, 64)
-    assert fa.launch_cfg(1, 8, n - 256, 64, False) == (1, 4, 64)      # 8 * (ceil(cus / 8) - 1) < cus
+    assert fa.launch_cfg(1, 8, 4 * n, 64, True) == (1, 8, 64)          # four layers of 256-query tiles
+    assert fa.launch_cfg(1, 8, n - 256, 64, False) == (1, 8, 64)      # 8-wave grid < cus < 4-wave grid
     assert fa.launch_cfg(1, 8, n - 256, 64, True) == ks
     m = 128 * ((cus + 7) // 8)                                         # 4-wave grid just fills the CUs
     assert fa.launch_cfg(1, 8, m, 64, False) == (1, 4, 64)
-    assert fa.launch_cfg(1, 8, m - 128, 64, False) == ks
+    assert fa.launch_cfg(1, 8, m // 2, 64, False) == ks                # ... or fills half of them
+    if cus == 256:
+        assert fa.launch_cfg(1, 8, n, 64, True) == (1, 4, 64)          # one layer: the longest tile sets the time
+        assert fa.launch_cfg(1, 8, m - 128, 64, False) == (1, 4, 64)
+
+
+# ---- a restatement of the causal rule ---------------------------------------
+FA_CAUSAL_GROUP = 2
+
+
+def causal_order(i, total, BH, nqt, res, cus):
+    """(head, query tile) of causal workgroup i: heads grouped per XCD, longest
+    tile first within groups of two heads, odd co-resident layers reversed."""
+    if BH % 8 == 0:
+        t = (i & 7) * (total >> 3) + (i >> 3)
+        per, hpx = total >> 3, BH >> 3
+        chunk, j = divmod(t, per)
+        cpx = cus >> 3
+        if res > 1 and cpx > 0 and cus % 8 == 0:
+            l, p = divmod(j, cpx)
+            if l % 2 == 1 and l < res and (l + 1) * cpx <= per:
+                j = l * cpx + (cpx - 1 - p)
+        gs = FA_CAUSAL_GROUP if hpx % FA_CAUSAL_GROUP == 0 else hpx
+        grp, r = divmod(j, gs * nqt)
+        return chunk * hpx + grp * gs + r % gs, nqt - 1 - r // gs
+    u = i
+    if res > 1 and cus > 0:
+        l, p = divmod(u, cus)
+        if l % 2 == 1 and l < res and (l + 1) * cus <= total:
+            u = l * cus + (cus - 1 - p)
+    return u % BH, nqt - 1 - u // BH
+
+
+def causal_balance(BH, N, rows, res, cus):
+    """Mean over largest per-CU count of visited 64-key tiles, per XCD: the first
+    res layers round-robin, then each workgroup on the least loaded CU."""
+    nqt = -(-N // rows)
+    total = BH * nqt
+    cpx = max(1, cus // 8)
+    worst = 1.0
+    for x in ([0] if BH % 8 == 0 and cus % 8 == 0 else range(8)):
+        work = [0] * cpx
+        for k, i in enumerate(range(x, total, 8)):
+            _, qt = causal_order(i, total, BH, nqt, res, cus)
+            c = k % cpx if k < cpx * res else work.index(min(work))
+            work[c] += -(-min(qt * rows + rows, N) // 64)
+        if max(work) > 0:
+            worst = min(worst, sum(work) / cpx / max(work))
+    return worst
+
+
+# Workgroups per CU of the causal 8- and 4-wavefront kernels (register and LDS
+# limits of the gfx950 build): d = 32 two and four, d = 64 one and three,
+# d = 128 one and two.
+RESIDENT = {32: (2, 4), 64: (1, 3), 128: (1, 2)}
+
+
+def causal_rule(B, H, N, d, cus):
+    w8, w4 = B * H * -(-N // 256), B * H * -(-N // 128)
+    if w8 >= 4 * cus:
+        return (1, 8, 64)
+    if (d <= 64 or w4 <= cus) if w8 < cus else (d == 32 and 2 * w8 <= 3 * cus):
+        return (1, 4, 32, 4)
+    r8, r4 = RESIDENT[d]
+    b8 = causal_balance(B * H, N, 256, r8, cus) if w8 >= cus else 0.0
+    if b8 >= 0.97 or causal_balance(B * H, N, 128, r4, cus) < b8:
+        return (1, 8, 64)
+    return (1, 4, 64)
+
+
+CAUSAL_SHAPES = [(4, 8, 2048), (2, 8, 4096), (1, 16, 4096), (1, 8, 8192), (3, 8, 4096), (4, 8, 3072), (4, 8, 4096),
+                 (2, 8, 8192), (8, 8, 2048), (5, 8, 4096), (6, 8, 4096), (4, 16, 4096), (8, 8, 1024), (16, 8, 512),
+                 (1, 32, 2048), (1, 24, 2048), (6, 8, 1024), (2, 12, 3000), (3, 5, 4096), (1, 32, 32768)]
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_causal_rule_matches_its_statement(d):
+    import torch
+    import flashattention_forward_fa2_amd as fa
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus != 256:
+        pytest.skip("the occupancy table above is MI355X's")
+    for B, H, N in CAUSAL_SHAPES:
+        want = causal_rule(B, H, N, d, cus)
+        for dt in ("bf16", "f16"):
+            assert fa.launch_cfg(B, H, N, d, True, dt) == want, (B, H, N, d, dt)
+
+
+def test_causal_choices_measured_on_mi355x():
+    """Where the tile sweeps put each causal shape (HIP events, best of the 8- and
+    4-wavefront tiles and the key split): the 8-wavefront tile only where its
+    order pairs long tiles with short ones on every CU."""
+    import torch
+    import flashattention_forward_fa2_amd as fa
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus != 256:
+        pytest.skip("measured on a 256-CU MI355X")
+    best = {(4, 8, 2048, 64): (1, 4, 64), (2, 8, 4096, 64): (1, 4, 64), (1, 8, 8192, 64): (1, 4, 64),
+            (3, 8, 4096, 64): (1, 4, 64), (4, 8, 3072, 64): (1, 8, 64), (4, 8, 4096, 64): (1, 8, 64),
+            (2, 8, 8192, 64): (1, 8, 64), (8, 8, 2048, 64): (1, 4, 64), (5, 8, 4096, 64): (1, 4, 64),
+            (6, 8, 4096, 64): (1, 4, 64), (16, 8, 512, 64): (1, 4, 64), (6, 8, 1024, 64): (1, 4, 32, 4),
+            (4, 8, 2048, 128): (1, 4, 64), (4, 8, 4096, 128): (1, 8, 64), (2, 8, 8192, 128): (1, 8, 64),
+            (8, 8, 1024, 128): (1, 4, 64), (1, 24, 2048, 128): (1, 4, 64), (1, 8, 4096, 128): (1, 4, 32, 4),
+            (1, 32, 32768, 128): (1, 8, 64), (4, 8, 2048, 32): (1, 4, 32, 4), (4, 8, 3072, 32): (1, 4, 32, 4),
+            (2, 16, 3072, 32): (1, 4, 32, 4), (8, 8, 2048, 32): (1, 8, 64), (4, 8, 4096, 32): (1, 8, 64)}
+    for (B, H, N, d), t in best.items():
+        assert fa.launch_cfg(B, H, N, d, True) == t == causal_rule(B, H, N, d, cus), (B, H, N, d)
 
 
 def balanced(B, H, N, waves, permille, cus):
@@ -72,7 +183,8 @@ def test_non_causal_tile_balances_the_compute_units(B, H, N, d):
     want = min(opts, key=lambda o: (balanced(B, H, N, o[0][1], o[1], cus), o[0] != (1, 8, 64)))[0]
     for dt in ("bf16", "f16"):
         assert fa.launch_cfg(B, H, N, d, False, dt) == want
-    assert fa.launch_cfg(B, H, N, d, True) in ((1, 8, 64),)                 # causal keeps the 8-wave tile
+    if cus == 256:
+        assert fa.launch_cfg(B, H, N, d, True) == causal_rule(B, H, N, d, cus)
     if cus == 256:                                                         # the measured choices on MI355X
         assert dict([((4, 8, 4096, 64), (1, 8, 64)), ((4, 8, 3072, 64), (1, 12, 64)),
                      ((4, 8, 6144, 64), (1, 12, 64)), ((4, 12, 2048, 64), (1, 4, 64)),
