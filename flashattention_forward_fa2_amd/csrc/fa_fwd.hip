@@ -277,7 +277,8 @@ double causal_balance(int BH, int Nq, int rows, int res, int cus) {
 // the 4-wavefront tile (1, 4, 64):
 // * Non-causal: the key-split tile (1, 4, 32, ksplit 4: four wavefronts share
 //   each block of 32 queries and split its keys) while 2*w4 <= CUs; (1, 4, 64)
-//   while w4 <= CUs; beyond, every query tile costs the same, so a launch lasts
+//   while w4 <= CUs (d = 32: while w8 <= CUs, five 4-wavefront workgroups fit
+//   a CU there); beyond, every query tile costs the same, so a launch lasts
 //   about as long as the busiest CU, which runs ceil(workgroups / CUs) tiles of
 //   `waves` wavefronts each: of the 8-, 12- (d = 64) and 4-wavefront tiles the
 //   one with the least such work, each weighed by its measured speed on grids
@@ -304,7 +305,7 @@ fa_tile_cfg launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, int c
   const Variant* v4 = find_variant(d, causal, four, dtype);
   if (!causal) {
     if (2 * w4 <= cus && has_ks) return ks;
-    if (w4 <= cus && v4) return four;
+    if ((w4 <= cus || (d == 32 && w8 <= cus)) && v4) return four;
     struct Option { fa_tile_cfg t; long long permille; };
     const Option opts[] = {{{1, 8, 64}, 1000}, {{1, 12, 64}, 975}, {{1, 4, 64}, d == 32 ? 1025 : d == 64 ? 1030 : 1050}};
     fa_tile_cfg best = c;

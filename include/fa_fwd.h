@@ -224,7 +224,8 @@ int fa_default_cfg(int N, int d, int causal, fa_tile_cfg *cfg);
  * tile.  At d = 32, 64 or 128 (bf16 or fp16), with w8 = B*H*ceil(Nq/256)
  * workgroups of (1, 8, 64) and w4 = B*H*ceil(Nq/128) of (1, 4, 64):
  * - non-causal: the key-split tile (1, 4, 32, ksplit 4) while 2*w4 <= CUs;
- *   (1, 4, 64) while w4 <= CUs; beyond, of (1, 8, 64), (1, 12, 64) (d = 64
+ *   (1, 4, 64) while w4 <= CUs (d = 32: while w8 <= CUs); beyond, of
+ *   (1, 8, 64), (1, 12, 64) (d = 64
  *   only) and (1, 4, 64) the tile that leaves the busiest compute unit the
  *   least work: ceil(workgroups / CUs) * waves, weighed by the tile's speed on
  *   evenly divided grids (8 waves 1.000, 12 waves 0.975, 4 waves 1.025 at

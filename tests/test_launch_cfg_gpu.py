@@ -1,7 +1,7 @@
 """The tile fa_fwd picks on its own (fa_launch_cfg), at d = 32, 64 and 128:
 non-causal, the key-split tile (four wavefronts sharing each 32-query block)
 while twice the 4-wavefront grid fits the compute units, the 4-wavefront tile
-while that grid does, and beyond the 8-, 12- or 4-wavefront tile that leaves the
+while that grid does (at d = 32 while the 8-wavefront grid does), and beyond the 8-, 12- or 4-wavefront tile that leaves the
 busiest compute unit the least work; causal, the key split on grids of fewer
 8-wavefront workgroups than compute units (at d = 128 only while the 4-wavefront
 grid fits them, at d = 32 up to 1.5 times the compute units), the 8-wavefront
@@ -57,6 +57,8 @@ def test_choice_follows_the_grid():
     if cus == 256:
         assert fa.launch_cfg(1, 8, n, 64, True) == (1, 4, 64)          # one layer: the longest tile sets the time
         assert fa.launch_cfg(1, 8, m - 128, 64, False) == (1, 4, 64)
+        assert fa.launch_cfg(4, 8, 2048, 32, False) == (1, 4, 64)      # d = 32: one layer of 8-wave tiles
+        assert fa.launch_cfg(4, 8, 2048, 64, False) == (1, 8, 64)
 
 
 # ---- a restatement of the causal rule ---------------------------------------
