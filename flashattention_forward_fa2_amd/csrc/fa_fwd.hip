@@ -286,8 +286,10 @@ double causal_balance(int BH, int Nq, int rows, int res, int cus) {
 //   4 waves 1025 at d = 32, 1030 at d = 64 and 1050 at d = 128); ties keep the
 //   8-wavefront tile.
 // * Causal: work per query tile grows along the diagonal.  The key-split tile
-//   while w8 < CUs (at d = 128 only while w4 <= CUs: its 128 KB of LDS leave one
-//   workgroup per CU; at d = 32, with 32 KB, up to w8 <= 1.5 CUs); (1, 8, 64)
+//   while w8 < CUs (at d = 128 only while w4 < CUs, or w4 = CUs with Nq >= 2048:
+//   its 128 KB of LDS leave one workgroup per CU, and four layers of short
+//   rows cost more than they balance; at d = 32, with 32 KB, up to w8 <= 1.5
+//   CUs); (1, 8, 64)
 //   from 4 layers of CUs on; in between (1, 8, 64)
 //   where its launch order loads the CUs evenly (causal_balance >= 0.97, e.g.
 //   two layers of tiles paired long with short), else (1, 4, 64), whose smaller
@@ -318,7 +320,8 @@ fa_tile_cfg launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, int c
     return best;
   }
   if (w8 >= 4LL * cus || !v4) return c;
-  if (has_ks && (w8 < cus ? d <= 64 || w4 <= cus : d == 32 && 2 * w8 <= 3LL * cus)) return ks;
+  if (has_ks && (w8 < cus ? d <= 64 || w4 < cus || (w4 == cus && Nq >= 2048) : d == 32 && 2 * w8 <= 3LL * cus))
+    return ks;
   // The balance replay costs a few microseconds; remember the last answers.
   struct Memo { long long bh; int nq, d, dtype, cus; fa_tile_cfg cfg; };
   thread_local Memo memo[8];

@@ -230,7 +230,8 @@ int fa_default_cfg(int N, int d, int causal, fa_tile_cfg *cfg);
  *   least work: ceil(workgroups / CUs) * waves, weighed by the tile's speed on
  *   evenly divided grids (8 waves 1.000, 12 waves 0.975, 4 waves 1.025 at
  *   d = 32, 1.030 at d = 64 and 1.050 at d = 128); ties keep (1, 8, 64);
- * - causal: the key-split tile while w8 < CUs (d = 128: while w4 <= CUs;
+ * - causal: the key-split tile while w8 < CUs (d = 128: while w4 < CUs, or
+ *   w4 = CUs with Nq >= 2048;
  *   d = 32: while w8 <= 1.5 CUs); (1, 8, 64) when w8 >= 4 CUs; in between
  *   (1, 8, 64) if its launch order, replayed on the host, loads the compute
  *   units evenly (mean over largest per-CU tile count >= 0.97) or more evenly

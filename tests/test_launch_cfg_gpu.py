@@ -4,7 +4,8 @@ while twice the 4-wavefront grid fits the compute units, the 4-wavefront tile
 while that grid does (at d = 32 while the 8-wavefront grid does), and beyond the 8-, 12- or 4-wavefront tile that leaves the
 busiest compute unit the least work; causal, the key split on grids of fewer
 8-wavefront workgroups than compute units (at d = 128 only while the 4-wavefront
-grid fits them, at d = 32 up to 1.5 times the compute units), the 8-wavefront
+grid is smaller, or just fills them with rows of 2048 or more; at d = 32 up to
+1.5 times the compute units), the 8-wavefront
 tile from four layers of them on, and in between the 8-wavefront tile only where
 its launch order loads the compute units evenly, else the 4-wavefront one.  The rule is checked against a Python
 restatement of it (its own replay of the causal launch order) and against the
@@ -116,7 +117,7 @@ def causal_rule(B, H, N, d, cus):
     w8, w4 = B * H * -(-N // 256), B * H * -(-N // 128)
     if w8 >= 4 * cus:
         return (1, 8, 64)
-    if (d <= 64 or w4 <= cus) if w8 < cus else (d == 32 and 2 * w8 <= 3 * cus):
+    if (d <= 64 or w4 < cus or (w4 == cus and N >= 2048)) if w8 < cus else (d == 32 and 2 * w8 <= 3 * cus):
         return (1, 4, 32, 4)
     r8, r4 = RESIDENT[d]
     b8 = causal_balance(B * H, N, 256, r8, cus) if w8 >= cus else 0.0
@@ -158,6 +159,7 @@ def test_causal_choices_measured_on_mi355x():
             (6, 8, 4096, 64): (1, 4, 64), (16, 8, 512, 64): (1, 4, 64), (6, 8, 1024, 64): (1, 4, 32, 4),
             (4, 8, 2048, 128): (1, 4, 64), (4, 8, 4096, 128): (1, 8, 64), (2, 8, 8192, 128): (1, 8, 64),
             (8, 8, 1024, 128): (1, 4, 64), (1, 24, 2048, 128): (1, 4, 64), (1, 8, 4096, 128): (1, 4, 32, 4),
+            (4, 8, 1024, 128): (1, 4, 64), (1, 4, 8192, 128): (1, 4, 32, 4), (4, 8, 512, 128): (1, 4, 32, 4),
             (1, 32, 32768, 128): (1, 8, 64), (4, 8, 2048, 32): (1, 4, 32, 4), (4, 8, 3072, 32): (1, 4, 32, 4),
             (2, 16, 3072, 32): (1, 4, 32, 4), (8, 8, 2048, 32): (1, 8, 64), (4, 8, 4096, 32): (1, 8, 64)}
     for (B, H, N, d), t in best.items():
