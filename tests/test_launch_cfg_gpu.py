@@ -14,8 +14,9 @@ the explicit launch of the configuration it names."""
 import numpy as np
 import pytest
 
+import oracle
 from inputs import random_qkv
-from parity import fp32_scale, to_device
+from parity import compare, fp32_scale, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -199,16 +200,23 @@ def test_non_causal_tile_balances_the_compute_units(B, H, N, d):
                      ((2, 16, 5000, 32), (1, 4, 64)), ((4, 8, 6144, 32), (1, 8, 64))])[(B, H, N, d)] == want
 
 
-@pytest.mark.parametrize("N,causal", [(1024, True), (1024, False), (4096, False), (300, True), (3072, False)])
+@pytest.mark.parametrize("N,causal", [(1024, True), (1024, False), (4096, False), (300, True), (3072, False),
+                                      (2048, True)])
 def test_default_launch_equals_the_named_configuration(N, causal):
     import torch
     import flashattention_forward_fa2_amd as fa
-    B, H = (4, 8) if N == 3072 else (1, 8)
+    B, H = (4, 8) if N in (3072, 2048) else (1, 8)
     d = 128 if N == 300 else 64
-    q, k, v = (to_device(a) for a in random_qkv(7700 + N, B, H, N, d))
+    qb, kb, vb = random_qkv(7700 + N, B, H, N, d)
+    q, k, v = (to_device(a) for a in (qb, kb, vb))
     scale = fp32_scale(d)
     o1, l1 = fa.fa_fwd(q, k, v, scale=scale, causal=causal)
     cfg = fa.launch_cfg(B, H, N, d, causal)
     o2, l2 = fa.fa_fwd(q, k, v, scale=scale, causal=causal, cfg=cfg)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    # and the default launch against the oracle on every 13th row (and the last)
+    rows = np.append(np.arange(0, B * H * N, 13), B * H * N - 1)
+    o_ref, l_ref = oracle.attention_rows(qb, kb, vb, scale, causal, rows=rows)
+    compare(o1.view(torch.int16).cpu().numpy().view(np.uint16), l1.cpu().numpy(), o_ref, l_ref, rows=rows,
+            label="default launch N=%d causal=%d cfg=%s" % (N, causal, cfg))
