@@ -429,7 +429,11 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
   if (j < ntiles) step(j, 0);
 
   // ---- epilogue: dK = scale * (dK^T)^T, dV -> E --------------------------------
-  const int key = kw + lr;
+  // The lane index is read again (mbcnt) rather than kept from the prologue, so
+  // that no per-lane value has to live across the query-tile loop.
+  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int g_e = lane_e >> 5;
+  const int key = kw + (lane_e & 31);
   if (key < Nk) {
     const int dk_rs = STRIDED ? pr.dk_rs : D, dv_rs = STRIDED ? pr.dv_rs : D;
     uint16_t* krow = pr.dk + head_off<STRIDED, D>(pr.dk_sb, pr.dk_sh, bh, pr.H, Nk) + (long long)key * dk_rs;
@@ -444,8 +448,8 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
         a[1] = E::pack(dk[db][4 * rr + 2] * sc, dk[db][4 * rr + 3] * sc);
         b[0] = E::pack(dv[db][4 * rr + 0], dv[db][4 * rr + 1]);
         b[1] = E::pack(dv[db][4 * rr + 2], dv[db][4 * rr + 3]);
-        *reinterpret_cast<u32x2*>(krow + db * 32 + 8 * rr + 4 * g) = a;
-        *reinterpret_cast<u32x2*>(vout + db * 32 + 8 * rr + 4 * g) = b;
+        *reinterpret_cast<u32x2*>(krow + db * 32 + 8 * rr + 4 * g_e) = a;
+        *reinterpret_cast<u32x2*>(vout + db * 32 + 8 * rr + 4 * g_e) = b;
       }
   }
 }
