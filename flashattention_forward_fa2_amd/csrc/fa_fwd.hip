@@ -155,6 +155,9 @@ const Variant kVariants[] = {
     // 12 wavefronts (three per SIMD) at d = 64, non-causal: grids that 384-query
     // tiles spread more evenly over the compute units than 256-query tiles
     FA_VARIANT(64, 0, 1, 12, 64), FA_VARIANT16(64, 0, 1, 12, 64),
+    // 32-key tiles at d = 64, non-causal: few enough registers for two 8-wavefront
+    // workgroups (four wavefronts) per SIMD
+    FA_VARIANT(64, 0, 1, 8, 32), FA_VARIANT16(64, 0, 1, 8, 32),
     // one wavefront of 32 queries: the split path's tile for decoding (Nq <= 32)
     FA_VARIANT(64, 0, 1, 1, 64), FA_VARIANT(64, 1, 1, 1, 64), FA_VARIANT(128, 0, 1, 1, 32),
     FA_VARIANT(128, 1, 1, 1, 32), FA_VARIANT16(64, 0, 1, 1, 64), FA_VARIANT16(64, 1, 1, 1, 64),
@@ -280,10 +283,12 @@ double causal_balance(int BH, int Nq, int rows, int res, int cus) {
 //   while w4 <= CUs (d = 32: while w8 <= CUs, five 4-wavefront workgroups fit
 //   a CU there); beyond, every query tile costs the same, so a launch lasts
 //   about as long as the busiest CU, which runs ceil(workgroups / CUs) tiles of
-//   `waves` wavefronts each: of the 8-, 12- (d = 64) and 4-wavefront tiles the
-//   one with the least such work, each weighed by its measured speed on grids
-//   that divide evenly (per mille of the 8-wavefront tile's time: 12 waves 975,
-//   4 waves 1025 at d = 32, 1030 at d = 64 and 1050 at d = 128); ties keep the
+//   `waves` wavefronts each: of the 8-, 12- (d = 64) and 4-wavefront tiles and
+//   the 8-wavefront tile with 32-key tiles (d = 64; 108 registers, so two of its
+//   workgroups share a CU) the one with the least such work, each weighed by its
+//   measured speed (per mille of the 8-wavefront tile's time: 12 waves 975,
+//   4 waves 1025 at d = 32, 1030 at d = 64 and 1050 at d = 128, 32-key tiles 970
+//   when some CU gets two workgroups and 1075 when none does); ties keep the
 //   8-wavefront tile.
 // * Causal: work per query tile grows along the diagonal.  The key-split tile
 //   while w8 < CUs (at d = 128 only while w4 < CUs, or w4 = CUs with Nq >= 2048:
@@ -308,13 +313,17 @@ fa_tile_cfg launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, int c
   if (!causal) {
     if (2 * w4 <= cus && has_ks) return ks;
     if ((w4 <= cus || (d == 32 && w8 <= cus)) && v4) return four;
-    struct Option { fa_tile_cfg t; long long permille; };
-    const Option opts[] = {{{1, 8, 64}, 1000}, {{1, 12, 64}, 975}, {{1, 4, 64}, d == 32 ? 1025 : d == 64 ? 1030 : 1050}};
+    // Per mille of the 8-wavefront tile's time per workgroup; the 32-key tile
+    // (d = 64) runs two workgroups per CU, faster once some CU gets two.
+    struct Option { fa_tile_cfg t; long long permille, permille_alone; };
+    const long long p4 = d == 32 ? 1025 : d == 64 ? 1030 : 1050;
+    const Option opts[] = {{{1, 8, 64}, 1000, 1000}, {{1, 8, 32}, 970, 1075}, {{1, 12, 64}, 975, 975}, {{1, 4, 64}, p4, p4}};
     fa_tile_cfg best = c;
     long long best_cost = -1;
     for (const Option& o : opts) {
       if (!find_variant(d, causal, o.t, dtype)) continue;
-      const long long cost = (wgs(o.t) + cus - 1) / cus * o.t.waves * o.permille;
+      const long long n = wgs(o.t);
+      const long long cost = (n + cus - 1) / cus * o.t.waves * (n > cus ? o.permille : o.permille_alone);
       if (best_cost < 0 || cost < best_cost) best_cost = cost, best = o.t;
     }
     return best;

@@ -225,11 +225,12 @@ int fa_default_cfg(int N, int d, int causal, fa_tile_cfg *cfg);
  * workgroups of (1, 8, 64) and w4 = B*H*ceil(Nq/128) of (1, 4, 64):
  * - non-causal: the key-split tile (1, 4, 32, ksplit 4) while 2*w4 <= CUs;
  *   (1, 4, 64) while w4 <= CUs (d = 32: while w8 <= CUs); beyond, of
- *   (1, 8, 64), (1, 12, 64) (d = 64
- *   only) and (1, 4, 64) the tile that leaves the busiest compute unit the
- *   least work: ceil(workgroups / CUs) * waves, weighed by the tile's speed on
- *   evenly divided grids (8 waves 1.000, 12 waves 0.975, 4 waves 1.025 at
- *   d = 32, 1.030 at d = 64 and 1.050 at d = 128); ties keep (1, 8, 64);
+ *   (1, 8, 64), (1, 8, 32) and (1, 12, 64) (d = 64 only) and (1, 4, 64) the
+ *   tile that leaves the busiest compute unit the least work: ceil(workgroups
+ *   / CUs) * waves, weighed by the tile's measured speed (8 waves 1.000, 12
+ *   waves 0.975, 4 waves 1.025 at d = 32, 1.030 at d = 64 and 1.050 at
+ *   d = 128; (1, 8, 32), whose workgroups run two per CU, 0.970 when the grid
+ *   has more workgroups than CUs, else 1.075); ties keep (1, 8, 64);
  * - causal: the key-split tile while w8 < CUs (d = 128: while w4 < CUs, or
  *   w4 = CUs with Nq >= 2048;
  *   d = 32: while w8 <= 1.5 CUs); (1, 8, 64) when w8 >= 4 CUs; in between
