@@ -294,12 +294,11 @@ double causal_balance(int BH, int Nq, int rows, int res, int cus) {
 //   while w8 < CUs (at d = 128 only while w4 < CUs, or w4 = CUs with Nq >= 2048:
 //   its 128 KB of LDS leave one workgroup per CU, and four layers of short
 //   rows cost more than they balance; at d = 32, with 32 KB, up to w8 <= 1.5
-//   CUs); (1, 8, 64)
-//   from 4 layers of CUs on; in between (1, 8, 64)
-//   where its launch order loads the CUs evenly (causal_balance >= 0.97, e.g.
-//   two layers of tiles paired long with short), else (1, 4, 64), whose smaller
-//   tiles and several workgroups per CU even out what one 256-query tile per CU
-//   cannot -- unless its own order balances worse.
+//   CUs); (1, 8, 64) from 4 layers of CUs on; in between (1, 8, 64) where its
+//   launch order loads the CUs evenly (causal_balance >= 0.97, e.g. two layers
+//   of tiles paired long with short), else (1, 4, 64), whose smaller tiles and
+//   several workgroups per CU even out what one 256-query tile per CU cannot --
+//   unless its own order balances worse.
 fa_tile_cfg launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, int cus) {
   const fa_tile_cfg c = default_cfg_dt(Nq, d, causal, dtype);
   if (c.waves != 8 || cus <= 0) return c;
