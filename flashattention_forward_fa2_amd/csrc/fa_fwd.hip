@@ -294,11 +294,13 @@ double causal_balance(int BH, int Nq, int rows, int res, int cus) {
 //   while w8 < CUs (at d = 128 only while w4 < CUs, or w4 = CUs with Nq >= 2048:
 //   its 128 KB of LDS leave one workgroup per CU, and four layers of short
 //   rows cost more than they balance; at d = 32, with 32 KB, up to w8 <= 1.5
-//   CUs); (1, 8, 64) from 4 layers of CUs on; in between (1, 8, 64) where its
-//   launch order loads the CUs evenly (causal_balance >= 0.97, e.g. two layers
-//   of tiles paired long with short), else (1, 4, 64), whose smaller tiles and
-//   several workgroups per CU even out what one 256-query tile per CU cannot --
-//   unless its own order balances worse.
+//   CUs).  Beyond, (1, 4, 64) where the 8-wavefront tile's launch order loads
+//   the CUs unevenly (causal_balance < 0.97: one layer of tiles, or groups of
+//   heads that do not pair long tiles with short ones), since its smaller tiles
+//   and several workgroups per CU even that out -- unless its own order balances
+//   worse; where both are even, (1, 8, 64), except from 4 layers on at d = 64
+//   (three 4-wavefront workgroups per CU against one of 8 wavefronts) and at
+//   d = 32 for rows up to 4096.
 fa_tile_cfg launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, int cus) {
   const fa_tile_cfg c = default_cfg_dt(Nq, d, causal, dtype);
   if (c.waves != 8 || cus <= 0) return c;
@@ -327,7 +329,7 @@ fa_tile_cfg launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, int c
     }
     return best;
   }
-  if (w8 >= 4LL * cus || !v4) return c;
+  if (!v4) return c;
   if (has_ks && (w8 < cus ? d <= 64 || w4 < cus || (w4 == cus && Nq >= 2048) : d == 32 && 2 * w8 <= 3LL * cus))
     return ks;
   // The balance replay costs a few microseconds; remember the last answers.
@@ -338,9 +340,20 @@ fa_tile_cfg launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, int c
   for (const Memo& m : memo)
     if (m.bh == BH && m.nq == Nq && m.d == d && m.dtype == dtype && m.cus == cus) return m.cfg;
   auto res = [](const Variant* v) { return v && v->resident ? v->resident() : 1; };
+  // Past 16 layers both orders are taken as even (the replay would cost more).
+  const bool replay = w8 <= 16LL * cus;
+  const double b8 = w8 < cus ? 0.0 : replay ? causal_balance((int)BH, Nq, 256, res(find_variant(d, causal, c, dtype)), cus) : 1.0;
+  const double b4 = replay ? causal_balance((int)BH, Nq, 128, res(v4), cus) : 1.0;
   fa_tile_cfg pick = four;
-  const double b8 = w8 >= cus ? causal_balance((int)BH, Nq, 256, res(find_variant(d, causal, c, dtype)), cus) : 0.0;
-  if (b8 >= 0.97 || causal_balance((int)BH, Nq, 128, res(v4), cus) < b8) pick = c;
+  if (b4 < b8) {
+    pick = c;
+  } else if (b8 >= 0.97) {
+    // Both even: from four layers on the 4-wavefront tile's extra workgroup
+    // per CU wins at d = 64 (three against two wavefronts per SIMD) and, for
+    // rows up to 4096, at d = 32; otherwise the 8-wavefront tile.
+    const bool long_grid = w8 >= 4LL * cus;
+    pick = long_grid && (d == 64 || (d == 32 && Nq <= 4096)) ? four : c;
+  }
   memo[memo_next] = Memo{BH, Nq, d, dtype, cus, pick};
   memo_next = (memo_next + 1) % 8;
   return pick;

@@ -232,11 +232,13 @@ int fa_default_cfg(int N, int d, int causal, fa_tile_cfg *cfg);
  *   d = 128; (1, 8, 32), whose workgroups run two per CU, 0.970 when the grid
  *   has more workgroups than CUs, else 1.075); ties keep (1, 8, 64);
  * - causal: the key-split tile while w8 < CUs (d = 128: while w4 < CUs, or
- *   w4 = CUs with Nq >= 2048;
- *   d = 32: while w8 <= 1.5 CUs); (1, 8, 64) when w8 >= 4 CUs; in between
- *   (1, 8, 64) if its launch order, replayed on the host, loads the compute
- *   units evenly (mean over largest per-CU tile count >= 0.97) or more evenly
- *   than (1, 4, 64)'s order does, else (1, 4, 64).  The last few answers are
+ *   w4 = CUs with Nq >= 2048; d = 32: while w8 <= 1.5 CUs); beyond, the launch
+ *   orders of (1, 8, 64) and (1, 4, 64) are replayed on the host (up to 16
+ *   layers of CUs; past that both count as even) and their balance (mean over
+ *   largest per-CU tile count) compared: (1, 8, 64) if its balance is above
+ *   (1, 4, 64)'s; else (1, 4, 64) if the balance of (1, 8, 64) is below 0.97;
+ *   else (both even) (1, 4, 64) from 4 layers of CUs on at d = 64, and at
+ *   d = 32 for Nq <= 4096, and (1, 8, 64) otherwise.  The last few answers are
  *   remembered per host thread.
  * FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_ARG (causal, dtype)
  * or FA_ERR_NO_DEVICE. */

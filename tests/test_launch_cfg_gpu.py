@@ -6,9 +6,10 @@ the 8-, 12- or 4-wavefront tile or the 32-key 8-wavefront tile, whichever leaves
 the busiest compute unit the least work.  Causal: the key split on grids of
 fewer 8-wavefront workgroups than compute units (at d = 128 only while the
 4-wavefront grid is smaller, or just fills them with rows of 2048 or more; at
-d = 32 up to 1.5 times the compute units), the 8-wavefront tile from four layers
-of them on, and in between the 8-wavefront tile only where its launch order
-loads the compute units evenly, else the 4-wavefront one.  The rule is checked
+d = 32 up to 1.5 times the compute units); beyond, the 4-wavefront tile where the
+8-wavefront tile's launch order loads the compute units unevenly (unless its own
+is worse), and where both are even the 8-wavefront tile, except from four layers
+on at d = 64 (and at d = 32 for rows up to 4096).  The rule is checked
 against a Python restatement of it (its own replay of the causal launch order)
 and against the choices tile sweeps measured on MI355X; the default launch is
 bit-identical to the explicit launch of the configuration it names."""
@@ -51,7 +52,8 @@ def test_choice_follows_the_grid():
     assert fa.launch_cfg(1, 8, 1024, 64, False, "f32") == (1, 4, 32)
     n = 256 * ((cus + 7) // 8)                                         # 8 heads x n/256 tiles >= cus
     assert fa.launch_cfg(1, 8, n, 64, False) == (1, 8, 64)
-    assert fa.launch_cfg(1, 8, 4 * n, 64, True) == (1, 8, 64)          # four layers of 256-query tiles
+    assert fa.launch_cfg(1, 8, 4 * n, 64, True) == (1, 4, 64)          # four layers: three 4-wave tiles per CU
+    assert fa.launch_cfg(1, 8, 4 * n, 128, True) == (1, 8, 64)         # ... at d = 128 two, as many as 8-wave ones
     assert fa.launch_cfg(1, 8, n - 256, 64, False) == (1, 8, 64)      # 8-wave grid < cus < 4-wave grid
     assert fa.launch_cfg(1, 8, n - 256, 64, True) == ks
     m = 128 * ((cus + 7) // 8)                                         # 4-wave grid just fills the CUs
@@ -117,15 +119,18 @@ RESIDENT = {32: (2, 4), 64: (1, 3), 128: (1, 2)}
 
 def causal_rule(B, H, N, d, cus):
     w8, w4 = B * H * -(-N // 256), B * H * -(-N // 128)
-    if w8 >= 4 * cus:
-        return (1, 8, 64)
     if (d <= 64 or w4 < cus or (w4 == cus and N >= 2048)) if w8 < cus else (d == 32 and 2 * w8 <= 3 * cus):
         return (1, 4, 32, 4)
     r8, r4 = RESIDENT[d]
-    b8 = causal_balance(B * H, N, 256, r8, cus) if w8 >= cus else 0.0
-    if b8 >= 0.97 or causal_balance(B * H, N, 128, r4, cus) < b8:
+    replay = w8 <= 16 * cus
+    b8 = 0.0 if w8 < cus else causal_balance(B * H, N, 256, r8, cus) if replay else 1.0
+    b4 = causal_balance(B * H, N, 128, r4, cus) if replay else 1.0
+    if b4 < b8:
         return (1, 8, 64)
-    return (1, 4, 64)
+    if b8 < 0.97:
+        return (1, 4, 64)
+    long_grid = w8 >= 4 * cus
+    return (1, 4, 64) if long_grid and (d == 64 or (d == 32 and N <= 4096)) else (1, 8, 64)
 
 
 CAUSAL_SHAPES = [(4, 8, 2048), (2, 8, 4096), (1, 16, 4096), (1, 8, 8192), (3, 8, 4096), (4, 8, 3072), (4, 8, 4096),
@@ -163,7 +168,11 @@ def test_causal_choices_measured_on_mi355x():
             (8, 8, 1024, 128): (1, 4, 64), (1, 24, 2048, 128): (1, 4, 64), (1, 8, 4096, 128): (1, 4, 32, 4),
             (4, 8, 1024, 128): (1, 4, 64), (1, 4, 8192, 128): (1, 4, 32, 4), (4, 8, 512, 128): (1, 4, 32, 4),
             (1, 32, 32768, 128): (1, 8, 64), (4, 8, 2048, 32): (1, 4, 32, 4), (4, 8, 3072, 32): (1, 4, 32, 4),
-            (2, 16, 3072, 32): (1, 4, 32, 4), (8, 8, 2048, 32): (1, 8, 64), (4, 8, 4096, 32): (1, 8, 64)}
+            (2, 16, 3072, 32): (1, 4, 32, 4), (8, 8, 2048, 32): (1, 8, 64), (4, 8, 4096, 32): (1, 8, 64),
+            (8, 16, 2048, 64): (1, 4, 64), (4, 32, 4096, 64): (1, 4, 64), (2, 16, 8192, 64): (1, 4, 64),
+            (1, 32, 32768, 64): (1, 4, 64), (16, 16, 2048, 64): (1, 4, 64), (8, 16, 2048, 128): (1, 4, 64),
+            (16, 16, 2048, 128): (1, 4, 64), (2, 16, 8192, 128): (1, 8, 64), (8, 8, 4096, 32): (1, 4, 64),
+            (4, 16, 8192, 32): (1, 8, 64), (16, 16, 2048, 32): (1, 4, 64), (1, 32, 32768, 32): (1, 8, 64)}
     for (B, H, N, d), t in best.items():
         assert fa.launch_cfg(B, H, N, d, True) == t == causal_rule(B, H, N, d, cus), (B, H, N, d)
 
