@@ -455,8 +455,11 @@ __global__ __launch_bounds__(WAVES * 64) void fa_bwd_dkdv_kernel(const BwdParams
 }
 
 // ---- dQ: one workgroup per WAVES*32 queries, key tiles of BK -----------------
+// Up to d = 64 the registers fit four wavefronts per SIMD (four workgroups per
+// CU): the non-causal kernel needs 134 VGPRs unconstrained and 124 when asked to.
 template <int D, bool CAUSAL, int WAVES, int BK, typename E = Bf16, bool STRIDED = false>
-__global__ __launch_bounds__(WAVES * 64) void fa_bwd_dq_kernel(const BwdParams pr) {
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 4 : 1)))
+void fa_bwd_dq_kernel(const BwdParams pr) {
   typedef typename E::v8 v8;
   constexpr int kBQ = WAVES * 32;
   constexpr int kTileBytes = BK * D * 2;  // one K or V tile
