@@ -279,7 +279,8 @@ double causal_balance(int BH, int Nq, int rows, int res, int cus) {
 // of the 8-wavefront tile (one per CU at a time) and w4 = B*H*ceil(Nq/128) of
 // the 4-wavefront tile (1, 4, 64):
 // * Non-causal: the key-split tile (1, 4, 32, ksplit 4: four wavefronts share
-//   each block of 32 queries and split its keys) while 2*w4 <= CUs; (1, 4, 64)
+//   each block of 32 queries and split its keys) while 2*w4 <= CUs (d = 128: its
+//   one workgroup per CU needs 4*w4 <= CUs, or rows of 1024 or more); (1, 4, 64)
 //   while w4 <= CUs (d = 32: while w8 <= CUs, five 4-wavefront workgroups fit
 //   a CU there); beyond, every query tile costs the same, so a launch lasts
 //   about as long as the busiest CU, which runs ceil(workgroups / CUs) tiles of
@@ -312,7 +313,7 @@ fa_tile_cfg launch_cfg(int B, int H, int Nq, int d, int causal, int dtype, int c
   const bool has_ks = find_variant(d, causal, ks, dtype) != nullptr;
   const Variant* v4 = find_variant(d, causal, four, dtype);
   if (!causal) {
-    if (2 * w4 <= cus && has_ks) return ks;
+    if (2 * w4 <= cus && has_ks && (d != 128 || 4 * w4 <= cus || Nq >= 1024)) return ks;
     if ((w4 <= cus || (d == 32 && w8 <= cus)) && v4) return four;
     // Per mille of the 8-wavefront tile's time per workgroup; the 32-key tile
     // (d = 64) runs two workgroups per CU, faster once some CU gets two.

@@ -223,8 +223,9 @@ int fa_default_cfg(int N, int d, int causal, fa_tile_cfg *cfg);
  * on the current device.  d = 256 and fp32 keep fa_default_cfg's 4-wavefront
  * tile.  At d = 32, 64 or 128 (bf16 or fp16), with w8 = B*H*ceil(Nq/256)
  * workgroups of (1, 8, 64) and w4 = B*H*ceil(Nq/128) of (1, 4, 64):
- * - non-causal: the key-split tile (1, 4, 32, ksplit 4) while 2*w4 <= CUs;
- *   (1, 4, 64) while w4 <= CUs (d = 32: while w8 <= CUs); beyond, of
+ * - non-causal: the key-split tile (1, 4, 32, ksplit 4) while 2*w4 <= CUs
+ *   (d = 128: and 4*w4 <= CUs or Nq >= 1024); (1, 4, 64) while w4 <= CUs
+ *   (d = 32: while w8 <= CUs); beyond, of
  *   (1, 8, 64), (1, 8, 32) and (1, 12, 64) (d = 64 only) and (1, 4, 64) the
  *   tile that leaves the busiest compute unit the least work: ceil(workgroups
  *   / CUs) * waves, weighed by the tile's measured speed (8 waves 1.000, 12

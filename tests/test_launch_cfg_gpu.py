@@ -63,6 +63,8 @@ def test_choice_follows_the_grid():
         assert fa.launch_cfg(1, 8, n, 64, True) == (1, 4, 64)          # one layer: the longest tile sets the time
         assert fa.launch_cfg(1, 8, m - 128, 64, False) == (1, 4, 64)
         assert fa.launch_cfg(4, 8, 2048, 32, False) == (1, 4, 64)      # d = 32: one layer of 8-wave tiles
+        assert fa.launch_cfg(4, 8, 512, 128, False) == (1, 4, 64)      # d = 128: two key-split layers of short rows
+        assert fa.launch_cfg(1, 8, 2048, 128, False) == ks             # ... of long rows
         assert fa.launch_cfg(4, 8, 2048, 64, False) == (1, 8, 64)
 
 
