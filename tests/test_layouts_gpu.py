@@ -130,30 +130,34 @@ def test_single_query_over_long_keys_equals_last_row():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_bnhd_on_the_twelve_wavefront_tile(dtype):
-    """[B, N, H, d] views at a non-causal shape whose default tile is the
-    12-wavefront one (B4 H8 N3072 d64 on a 256-CU device: 256 workgroups of 384
-    queries), so the strided instantiation of that tile runs; sampled rows
-    (every 384-query tile's edges and the ragged last one) against the oracle,
+@pytest.mark.parametrize("N,tile", [(3072, (1, 12, 64)), (4096, (1, 8, 32))])
+def test_bnhd_on_the_default_non_causal_tiles(N, tile, dtype):
+    """[B, N, H, d] views at non-causal shapes whose default tiles on a 256-CU
+    device are the 12-wavefront one (B4 H8 N3072 d64: 256 workgroups of 384
+    queries) and the 32-key 8-wavefront one (B4 H8 N4096 d64: 512 workgroups of
+    256 queries, two per CU), so the strided instantiations of those tiles run;
+    sampled rows (every query tile's edges and the last row) against the oracle,
     and bit-identity with the contiguous launch of the same tile."""
     import torch
     import flashattention_forward_fa2_amd as fa
     from inputs import sample_rows
-    B, H, N, d = 4, 8, 3072, 64
+    B, H, d = 4, 8, 64
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     cfg = fa.launch_cfg(B, H, N, d, False, dtype)
     if cus == 256:
-        assert cfg == (1, 12, 64)
-    q, k, v = random_qkv(6600, B, H, N, d, dtype=dtype)
+        assert cfg == tile
+    q, k, v = random_qkv(6600 + N, B, H, N, d, dtype=dtype)
     tq, tk, tv = (to_device(a, dtype=dtype).permute(0, 2, 1, 3).contiguous() for a in (q, k, v))  # [B, N, H, d]
     out, lse = run_ex(tq.transpose(1, 2), tk.transpose(1, 2), tv.transpose(1, 2), fp32_scale(d), False)
-    rows = sample_rows(6600, B, H, N, per_head=24)
-    extra = np.array([bh * N + i for bh in range(B * H) for i in (383, 384, 767, 768, 2687, 2688)])
+    rows = sample_rows(6600 + N, B, H, N, per_head=24)
+    bq = 32 * cfg[0] * cfg[1]
+    edges = sorted({i for t in range(0, N, bq) for i in (t, min(t + bq, N) - 1)})
+    extra = np.array([bh * N + i for bh in range(B * H) for i in edges[:4] + edges[-2:]])
     rows = np.unique(np.concatenate([rows, extra]))
     o_ref, l_ref = oracle.attention_rows(q, k, v, fp32_scale(d), False, rows=rows, dtype=dtype)
     tol = dict(o_max=4e-3, o_mean=3e-4) if dtype == "f16" else {}
     compare(bits_of(out), lse.contiguous().cpu().numpy(), o_ref, l_ref, rows=rows, dtype=dtype,
-            label="bnhd 12-wave tile %s" % dtype, **tol)
+            label="bnhd tile %s N=%d %s" % (cfg, N, dtype), **tol)
     o2, l2 = fa.fa_fwd_ex(to_device(q, dtype=dtype), to_device(k, dtype=dtype), to_device(v, dtype=dtype),
                           scale=fp32_scale(d), causal=False, cfg=cfg)
     torch.cuda.synchronize()
