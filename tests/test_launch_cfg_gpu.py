@@ -179,6 +179,20 @@ def test_causal_choices_measured_on_mi355x():
         assert fa.launch_cfg(B, H, N, d, True) == t == causal_rule(B, H, N, d, cus), (B, H, N, d)
 
 
+def test_rule_answers_do_not_depend_on_call_order():
+    """The causal answers are remembered (eight per host thread): asking for more
+    shapes than that, in one order, in reverse and again, with both element
+    types interleaved, gives the same tiles every time."""
+    import flashattention_forward_fa2_amd as fa
+    shapes = [(B, H, N, d) for (B, H, N) in CAUSAL_SHAPES[:12] for d in (64, 128)]
+    first = {(sh, dt): fa.launch_cfg(*sh, True, dt) for sh in shapes for dt in ("bf16", "f16")}
+    for order in (shapes[::-1], shapes[::3] + shapes[1::3] + shapes[2::3]):
+        for sh in order:
+            for dt in ("f16", "bf16"):
+                assert fa.launch_cfg(*sh, True, dt) == first[(sh, dt)], (sh, dt)
+    assert all(first[(sh, "bf16")] == first[(sh, "f16")] for sh in shapes)
+
+
 def balanced(B, H, N, waves, permille, cus):
     """Work of the busiest compute unit, weighed per mille; permille is a pair
     (the tile's weight once some CU gets two workgroups, and before)."""
