@@ -79,6 +79,8 @@ def parse():
                     help="element type of q, k, v, out (f16 and f32 run through fa_fwd_ex)")
     ap.add_argument("--headdim", type=int, default=None, choices=[32, 64, 128, 256],
                     help="override the workload's head dimension (same B, H, N and distributions)")
+    ap.add_argument("--seq-len", type=int, default=None,
+                    help="override the workload's sequence length N (same B, H, d and distributions)")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward (fa_bwd: dQ, dK, dV from the forward's out and LSE) instead")
     ap.add_argument("--no-extra", action="store_true",
@@ -137,6 +139,9 @@ def main():
     if args.headdim:
         w["d"] = args.headdim
         w["name"] = re.sub(r"-d\d+", "-d%d" % args.headdim, w["name"])
+    if args.seq_len:
+        w["N"] = args.seq_len
+        w["name"] = re.sub(r"-N\d+", "-N%d" % args.seq_len, w["name"])
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
     modes = list(w["modes"]) if args.workload != 3 else [0, 1]
     if args.only:
@@ -301,7 +306,8 @@ def main():
     if cpu is not None:
         rec["vs_cpu_baseline"] = round(value / cpu["value"], 1)
     default_run = (args.workload == 3 and args.layout == "bhnd" and args.nq is None and args.splitkv is None
-                   and args.dtype == "bf16" and not args.headdim and not args.cfg and not args.only)
+                   and args.dtype == "bf16" and not args.headdim and not args.seq_len and not args.cfg
+                   and not args.only)
     if default_run and not args.no_extra:
         del q, k, v, outs, lses
         torch.cuda.empty_cache()
@@ -414,6 +420,9 @@ def main_bwd(args):
     if args.headdim:
         w["d"] = args.headdim
         w["name"] = re.sub(r"-d\d+", "-d%d" % args.headdim, w["name"])
+    if args.seq_len:
+        w["N"] = args.seq_len
+        w["name"] = re.sub(r"-N\d+", "-N%d" % args.seq_len, w["name"])
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
     modes = list(w["modes"]) if args.workload != 3 else [0, 1]
     if args.only:
