@@ -153,7 +153,7 @@ def main():
     cfg = tuple(int(x) for x in args.cfg.split(",")) if args.cfg else None
 
     t0 = time.time()
-    q_bits, k_bits, v_bits = inputs.make_qkv(args.workload, d=d, dtype=args.dtype)
+    q_bits, k_bits, v_bits = inputs.make_qkv(args.workload, N=N, d=d, dtype=args.dtype)
     print("[bench] inputs %s generated in %.1fs" % (w["name"], time.time() - t0), file=sys.stderr, flush=True)
     Nk = N
     if args.nq is not None:
@@ -428,7 +428,7 @@ def main_bwd(args):
     if args.only:
         modes = [c for c in modes if c == (args.only == "causal")]
     scale = inputs.default_scale(d)
-    q_bits, k_bits, v_bits = inputs.make_qkv(args.workload, d=d, dtype=args.dtype)
+    q_bits, k_bits, v_bits = inputs.make_qkv(args.workload, N=N, d=d, dtype=args.dtype)
     g_bits = inputs.normal_bits(inputs.workload_seed(args.workload, 4), B * H * N * d,
                                 dtype=args.dtype).reshape(B, H, N, d)
     tdt = torch.float16 if args.dtype == "f16" else torch.bfloat16
