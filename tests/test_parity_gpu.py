@@ -74,6 +74,22 @@ def test_every_compiled_variant(variant):
     check_rows(q, k, v, fp32_scale(d), causal, cfg=cfg, label="variant d=%d c=%d %s" % (d, causal, cfg))
 
 
+@pytest.mark.parametrize("B,H,N,d", [(1, 32, 32768, 64), (16, 16, 2048, 128)])
+def test_long_causal_grids_on_the_default_tile(B, H, N, d):
+    """Causal grids of many layers whose default tile on a 256-CU device is the
+    4-wavefront one (the long-context shape at d = 64; B16-H16-N2048 at d = 128,
+    where the 8-wavefront order loads the CUs unevenly): 24 sampled rows per head
+    plus each head's first and last rows, against the oracle."""
+    import torch
+    import flashattention_forward_fa2_amd as fa
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert fa.launch_cfg(B, H, N, d, True) == (1, 4, 64)
+    q, k, v = random_qkv(9400 + d, B, H, N, d)
+    rows = sample_rows(9400 + d, B, H, N, per_head=24)
+    rows = np.unique(np.concatenate([rows, np.arange(B * H) * N, np.arange(1, B * H + 1) * N - 1]))
+    check_rows(q, k, v, fp32_scale(d), 1, rows=rows, label="long causal B%d H%d N%d d%d default" % (B, H, N, d))
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [0, 1])
 def test_identical_keys_average_the_values(d, causal):
